@@ -1,0 +1,70 @@
+"""Accuracy of the quantized contract on the named workloads at their full
+sizes: on each workload's oracle subset (all heads, 8 seeded heads, or 16
+seeded 64-row query blocks), the oracle's bf16 output against brute-force
+fp64 attention of the same bf16 inputs.
+
+Bar: cosine >= 0.995 per checked head or block. The Student-t outlier
+workload does not reach it: measured per-block cosines run from 0.918 to
+0.998 (min 0.9183 on block (3, 15, 127), whose Q block absmax is 40.5 and
+whose K blocks reach absmax 860). There the oracle's output matches fp64
+attention on its own dequantized operands to cosine >= 0.9999 on every
+block, so the loss is the 64-row INT8 block contract on heavy-tailed data,
+not the epoch loop; that workload asserts the dequantized match and records
+its measured level with a floor of 0.9.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+
+
+def _cos(a, b):
+    a = a.ravel().astype(np.float64)
+    b = b.ravel().astype(np.float64)
+    return float(a @ b / math.sqrt((a @ a) * (b @ b)))
+
+
+def _check_item(w, q, k, v, b, h, rows, dequantized=False):
+    qb, kb, vb = (si.bf16_bits(t[b, h]) for t in (q, k, v))
+    p = oracle.prep_head(qb, kb, vb)
+    assert p["exact_mean"]
+    r0, r1 = rows
+    out = oracle.bf16_to_f32(oracle.attn_rows(p, w.causal, w.sm_scale, r0, r1))
+    qf, kf, vf = (oracle.bf16_to_f32(x).astype(np.float64) for x in (qb, kb, vb))
+    ref = oracle.attn_ref(qf, kf, vf, w.causal, w.sm_scale, r0, r1)
+    if not dequantized:
+        return _cos(out, ref), 1.0
+    Lq, Lkv = w.Lq, w.Lkv
+    qd = p["q8"][:Lq].astype(np.float64) * np.repeat(p["q_scale"], 64)[:Lq, None]
+    kd = p["k8"][:Lkv].astype(np.float64) * np.repeat(p["k_scale"], 64)[:Lkv, None] + p["k_mean"][None, :]
+    vd = oracle.e4m3_decode(p["v8"][:Lkv]) * p["v_scale"][None, :]
+    deq = oracle.attn_ref(qd, kd, vd, w.causal, w.sm_scale, r0, r1)
+    return _cos(out, ref), _cos(out, deq)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_workload_oracle_subset_accuracy(idx):
+    w = si.WORKLOADS[idx]
+    q, k, v = si.workload_qkv(w)
+    kind, _ = w.oracle_subset
+    if kind == "blocks":
+        items = [(b, h, (qb * 64, min(w.Lq, qb * 64 + 64))) for (b, h, qb) in si.oracle_blocks(w)]
+    else:
+        items = [(b, h, (0, w.Lq)) for (b, h) in si.oracle_heads(w)]
+    # split full heads into row chunks so every core has work
+    work = []
+    for (b, h, (r0, r1)) in items:
+        step = 512
+        work += [(b, h, (a, min(a + step, r1))) for a in range(r0, r1, step)]
+    outlier = w.dist == "student_t_outlier"
+    res = oracle.run_heads(lambda it: _check_item(w, q, k, v, *it, dequantized=outlier), work)
+    cos = [r[0] for r in res]
+    print(f"{w.name}: min cosine {min(cos):.5f} over {len(work)} row chunks")
+    if outlier:
+        assert min(r[1] for r in res) >= 0.9999
+        assert min(cos) >= 0.9
+    else:
+        assert min(cos) >= 0.995
