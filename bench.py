@@ -1,0 +1,173 @@
+"""Throughput of the quantized attention path on one MI355X.
+
+One step = the whole path on one batch: sage_quant_prep (K mean, smoothing,
+INT8 Q/K blocks, FP8 V) followed by sage_attn_fwd_prepped (the fused main
+loop), on inputs already resident in HBM. Prints one JSON line.
+
+  value     whole-step throughput in TOPS, ops = 4*B*H*Lq*Lkv*D (halved when
+            causal), over the wall time of K steps between two device syncs;
+  roofline  the main kernel: the same ops over its average launch duration
+            (HIP events around each main launch inside the timed steps,
+            recorded on the stream the kernels run on), against the dense
+            INT8/FP8 matrix-core peak of MI355X (5.0 POPS);
+  cpu_baseline  the CPU oracle (prep + epoch loop) on a bounded sample: one
+            full (b, h) head, rows spread over the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "INT8/FP8 attention TOPS & % MFMA peak, B2 H32 L4096 D128 causal"
+PEAK_TOPS = 5000.0       # MI355X dense INT8 / FP8 matrix-core peak
+HBM_PEAK_GBS = 8000.0
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_exact_attention_smooth_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per main-kernel launch from the committed counter summary,
+    only if it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("src_hash") != _src_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w) -> dict:
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+
+    threads = oracle.default_threads()
+    q, k, v = si.make_qkv(1, 1, w.Lq, w.Lkv, w.D, w.dist, w.k_offset_sigma, seed=1000)
+    qb, kb, vb = (si.bf16_bits(t[0, 0]) for t in (q, k, v))
+    t0 = time.perf_counter()
+    p = oracle.prep_head(qb, kb, vb)
+    oracle.attn_rows_parallel(p, w.causal, w.sm_scale, 0, w.Lq, threads=threads, chunk=64)
+    dt = time.perf_counter() - t0
+    ops = 4.0 * w.Lq * w.Lkv * w.D / (2 if w.causal else 1)
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"one (b,h) head of {w.name}: preparation + all {w.Lq} query rows, "
+                      f"{dt:.2f} s wall on {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=None, help="index into seeded_inputs.WORKLOADS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards over (b, h) heads with no exchange, see DESIGN.md", file=sys.stderr)
+        return 3
+
+    import torch
+    import seeded_inputs as si
+    from quantized_exact_attention_smooth_amd import _lib
+
+    w = si.WORKLOADS[si.HEADLINE if args.workload is None else args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in si.workload_qkv(w))
+    B, H, Lq, Lkv, D = w.B, w.H, w.Lq, w.Lkv, w.D
+    L = _lib.lib()
+    nqb, nkb = -(-Lq // 64), -(-Lkv // 64)
+    # prepared operands and scratch, allocated once
+    q8 = torch.empty((B, H, nqb * 64, D), dtype=torch.int8, device=dev)
+    qs = torch.empty((B, H, nqb), dtype=torch.float32, device=dev)
+    k8 = torch.empty((B, H, nkb * 64, D), dtype=torch.int8, device=dev)
+    kscale = torch.empty((B, H, nkb), dtype=torch.float32, device=dev)
+    kmean = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    v8 = torch.empty((B, H, nkb, D, 64), dtype=torch.uint8, device=dev)
+    vscale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    n = ctypes.c_size_t(0)
+    _lib.check("sage_prep_scratch_bytes", L.sage_prep_scratch_bytes(B, H, Lq, Lkv, D, ctypes.byref(n)))
+    scratch = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, Lq, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    causal = int(w.causal)
+
+    def prep():
+        _lib.check("sage_quant_prep", L.sage_quant_prep(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Lq, Lkv, D, q8.data_ptr(), qs.data_ptr(),
+            k8.data_ptr(), kscale.data_ptr(), kmean.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
+            scratch.data_ptr(), n.value, sp))
+
+    def main_loop():
+        _lib.check("sage_attn_fwd_prepped", L.sage_attn_fwd_prepped(
+            q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), kscale.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
+            out.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale, sp))
+
+    for _ in range(args.warmup):
+        prep()
+        main_loop()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        prep()
+        ev[i][1].record(stream)
+        main_loop()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prep_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    main_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_step = wall * 1e3 / K
+    ops = w.metric_ops
+    main_avg = sum(main_ms) / K
+    prep_avg = sum(prep_ms) / K
+    achieved = ops / (main_avg * 1e-3) / 1e12
+    med = sorted(main_ms)[K // 2]
+    prep_bytes = B * H * (Lq + 2 * Lkv) * D * 2 + B * H * (nqb + 2 * nkb) * 64 * D
+
+    rec = {
+        "metric": METRIC, "value": ops / (ms_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8+fp8_e4m3", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "Lq": Lq, "Lkv": Lkv, "D": D, "causal": w.causal,
+                   "k_offset_sigma": w.k_offset_sigma, "dist": w.dist},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_TOPS, "traffic": _traffic(w.name)},
+        "main_ms": main_avg, "main_ms_p50": med, "main_tops": achieved,
+        "prep_ms": prep_avg, "prep_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9,
+        "prep_frac_hbm": prep_bytes / (prep_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,135 @@
+/*
+ * sage_attn.h - C ABI of the MI355X (gfx950) quantized exact attention library.
+ *
+ * The method is SageAttention2-style quantized attention with K smoothing, as
+ * the "Experiment Log" page (vortex_exact_attention) lists its contract in
+ * section "Phase 0 Import And Verification": Q/K preparation, K smoothing,
+ * INT8 quantization, QK traversal, online softmax, FP8 V/P, two-level PV
+ * accumulation, final conversion and ragged tails. Section "Phase 1
+ * State-Ownership Decision" adds strict tile order, exact FP8 score bytes and
+ * per-tile RO rescaling.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers to tensors are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or keeps a pointer after a call returns.
+ *  - q is [B][H][Lq][D], k, v are [B][H][Lkv][D], out is [B][H][Lq][D]:
+ *    bf16 (raw 16-bit storage), D contiguous, base address 16-byte aligned.
+ *  - D is 64 or 128; B, H, Lq, Lkv >= 1; B*H*max(Lq,Lkv)*D < 2^40.
+ *  - Quantization blocks and attention epochs are SAGE_BLOCK = 64 rows/keys;
+ *    NQB = ceil(Lq/64), NKB = ceil(Lkv/64).
+ *  - stream is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *    work; results are valid once the stream has synchronised. Calls keep no
+ *    state between them and may be made from several host threads.
+ *  - Arguments are validated before any GPU call; on an error nothing is
+ *    enqueued. A failed launch is reported as SAGE_ERR_HIP. NaN or Inf inputs
+ *    give unspecified output values, never a fault.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_BLOCK 64
+
+enum sage_status {
+    SAGE_OK = 0,
+    SAGE_ERR_INVALID_ARG = -1, /* null or misaligned pointer, size < 1, bad flag */
+    SAGE_ERR_UNSUPPORTED = -2, /* D not in {64, 128} */
+    SAGE_ERR_WORKSPACE = -3,   /* workspace or scratch too small */
+    SAGE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/* Human-readable name of a status code (static storage). */
+const char* sage_status_str(int status);
+
+/*
+ * Bytes of device scratch sage_quant_prep needs (fp64 channel partial sums
+ * and fp32 channel absmax partials). Host-only; writes *bytes.
+ */
+int sage_prep_scratch_bytes(int B, int H, int Lq, int Lkv, int D, size_t* bytes);
+
+/*
+ * Bytes of device workspace sage_attn_fwd needs: every output of
+ * sage_quant_prep laid out as below, each part 256-byte aligned, followed by
+ * the preparation scratch. Host-only; writes *bytes.
+ */
+int sage_workspace_bytes(int B, int H, int Lq, int Lkv, int D, size_t* bytes);
+
+/*
+ * Preparation pass (Experiment Log, "Phase 0 Import And Verification":
+ * Q/K preparation, K smoothing, INT8 quantization, FP8 V).
+ * Inputs q, k, v as above. Outputs (device, caller-owned):
+ *   k_mean  fp32 [B][H][D]        mean[c] = fp32(fp64 sum_t K[t][c] / Lkv)
+ *   k_i8    int8 [B][H][NKB*64][D] codes of Ks = fp32(K) - mean, per 64-row
+ *                                  block: s = absmax/127, code =
+ *                                  clamp(rint_even(Ks / s), -127, 127)
+ *   k_scale fp32 [B][H][NKB]
+ *   q_i8    int8 [B][H][NQB*64][D] the same block codes of raw Q
+ *   q_scale fp32 [B][H][NQB]
+ *   v_scale fp32 [B][H][D]         sv[c] = max_t |V[t][c]| / 448
+ *   v_fp8   uint8 [B][H][NKB][D][64] E4M3FN codes of V / sv (nearest-even,
+ *                                  saturating), stored per 64-key block with
+ *                                  the keys of a channel contiguous
+ * Padded rows/keys (beyond Lq or Lkv) hold code 0; an all-zero block or
+ * channel has scale 0 and codes 0. The int8 outputs and v_fp8 must be 16-byte
+ * aligned. scratch: device memory of at least sage_prep_scratch_bytes; its
+ * contents on entry do not matter.
+ */
+int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
+                    int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                    uint8_t* v_fp8, float* v_scale, void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Attention from prepared operands (the fused main loop alone), in the
+ * layouts sage_quant_prep writes. Per query row i, strictly ascending 64-key
+ * epochs (Experiment Log, "Phase 1 State-Ownership Decision"):
+ *   S = q8 . k8 (exact int32), z = S * sq * sk * sm_scale, online max m and
+ *   sum l, alpha = exp(m_old - m_new), P8 = e4m3(exp(z - m_new)),
+ *   PV = P8 . V8 (fp32, one epoch), RO = RO * alpha + PV;
+ *   out = bf16(RO * (1/l) * sv[c])   ("reciprocal" then BF16; Experiment
+ *   Log, "Phase 2B Fixed Aligned Numerical Prototype").
+ * causal = 1 masks key j > i + Lkv - Lq (bottom-right aligned); a row with no
+ * visible key outputs 0. sm_scale <= 0 selects 1/sqrt(D). out is written for
+ * rows < Lq only.
+ */
+int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                          const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
+                          int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, void* stream);
+
+/*
+ * The whole path: sage_quant_prep into the workspace, then
+ * sage_attn_fwd_prepped. workspace: device memory of at least
+ * sage_workspace_bytes, 256-byte aligned; it is overwritten.
+ */
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
+                  int D, int causal, float sm_scale, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * Debug: the exact int32 QK accumulators of chosen 64x64 tiles, computed by
+ * the same LDS staging and INT8 matrix-core code as the main loop
+ * (Experiment Log, "Phase 2B": the "QK" checkpoint).
+ * tiles: HOST array of n_tiles records {b, h, query block, key block}, each
+ * checked against B, H, NQB, NKB. acc_out: device int32 [n_tiles][64][64],
+ * row = query within the block, column = key within the block.
+ */
+int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int Lq, int Lkv, int D,
+                        const int* tiles, int n_tiles, int32_t* acc_out, void* stream);
+
+/*
+ * Debug: run the device conversions the main loop uses on n fp32 values x
+ * (device): p8[i] = FP8 E4M3FN code as the probability packing produces it,
+ * bf16[i] = bf16 bits as the output conversion produces them.
+ */
+int sage_debug_codecs(const float* x, int n, uint8_t* p8, uint16_t* bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_ATTN_H */

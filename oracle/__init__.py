@@ -80,10 +80,16 @@ def _c(a, dtype):
 
 
 def default_threads() -> int:
+    """Cores this process may use, capped by OMP_NUM_THREADS when it is set
+    (the machine's share can be smaller than what the kernel reports)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 # ----------------------------------------------------------------- codecs

@@ -1,0 +1,142 @@
+"""MI355X (gfx950) SageAttention2-style quantized exact attention with K smoothing.
+
+Python face of the C ABI in include/sage_attn.h (same names, torch tensors in
+place of raw pointers). Inputs are bf16 CUDA tensors [B, H, L, D] with D in
+{64, 128}; outputs are allocated with torch on the same device; calls run on
+torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import (LIB_PATH, SAGE_BLOCK, SageError, check, lib, status_str)  # noqa: F401
+
+__all__ = ["workspace_bytes", "prep_scratch_bytes", "quant_prep", "attn_fwd_prepped", "attn_fwd",
+           "debug_qk_int32", "debug_codecs", "SageError", "status_str", "LIB_PATH"]
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    return t.data_ptr()
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, D]")
+    B, H, Lq, D = q.shape
+    Lkv = k.shape[2]
+    if tuple(k.shape) != (B, H, Lkv, D):
+        raise ValueError("k must be [B, H, Lkv, D] matching q")
+    return B, H, Lq, Lkv, D
+
+
+def workspace_bytes(B: int, H: int, Lq: int, Lkv: int, D: int) -> int:
+    n = ctypes.c_size_t(0)
+    check("sage_workspace_bytes", lib().sage_workspace_bytes(B, H, Lq, Lkv, D, ctypes.byref(n)))
+    return n.value
+
+
+def prep_scratch_bytes(B: int, H: int, Lq: int, Lkv: int, D: int) -> int:
+    n = ctypes.c_size_t(0)
+    check("sage_prep_scratch_bytes", lib().sage_prep_scratch_bytes(B, H, Lq, Lkv, D, ctypes.byref(n)))
+    return n.value
+
+
+def quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, stream=None) -> dict:
+    """sage_quant_prep. Returns dict of q_i8, q_scale, k_i8, k_scale, k_mean,
+    v_fp8 ([B, H, NKB, D, 64] uint8), v_scale and the shape."""
+    B, H, Lq, Lkv, D = _dims(q, k)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must match k")
+    nqb, nkb = -(-Lq // SAGE_BLOCK), -(-Lkv // SAGE_BLOCK)
+    dev = q.device
+    r = dict(q_i8=torch.empty((B, H, nqb * SAGE_BLOCK, D), dtype=torch.int8, device=dev),
+             q_scale=torch.empty((B, H, nqb), dtype=torch.float32, device=dev),
+             k_i8=torch.empty((B, H, nkb * SAGE_BLOCK, D), dtype=torch.int8, device=dev),
+             k_scale=torch.empty((B, H, nkb), dtype=torch.float32, device=dev),
+             k_mean=torch.empty((B, H, D), dtype=torch.float32, device=dev),
+             v_fp8=torch.empty((B, H, nkb, D, SAGE_BLOCK), dtype=torch.uint8, device=dev),
+             v_scale=torch.empty((B, H, D), dtype=torch.float32, device=dev))
+    nbytes = prep_scratch_bytes(B, H, Lq, Lkv, D)
+    scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().sage_quant_prep(_dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
+                               _dev(v, torch.bfloat16, "v"), B, H, Lq, Lkv, D,
+                               r["q_i8"].data_ptr(), r["q_scale"].data_ptr(), r["k_i8"].data_ptr(),
+                               r["k_scale"].data_ptr(), r["k_mean"].data_ptr(), r["v_fp8"].data_ptr(),
+                               r["v_scale"].data_ptr(), scratch.data_ptr(), nbytes, _stream(stream))
+    check("sage_quant_prep", st)
+    r["_scratch"] = scratch  # keep alive until the stream is done with it
+    r["shape"] = (B, H, Lq, Lkv, D)
+    return r
+
+
+def attn_fwd_prepped(prep: dict, causal: bool, sm_scale: float = None, out: torch.Tensor = None,
+                     stream=None) -> torch.Tensor:
+    """sage_attn_fwd_prepped on the dict quant_prep returns."""
+    B, H, Lq, Lkv, D = prep["shape"]
+    if out is None:
+        out = torch.empty((B, H, Lq, D), dtype=torch.bfloat16, device=prep["q_i8"].device)
+    st = lib().sage_attn_fwd_prepped(
+        _dev(prep["q_i8"], torch.int8, "q_i8"), _dev(prep["q_scale"], torch.float32, "q_scale"),
+        _dev(prep["k_i8"], torch.int8, "k_i8"), _dev(prep["k_scale"], torch.float32, "k_scale"),
+        _dev(prep["v_fp8"], torch.uint8, "v_fp8"), _dev(prep["v_scale"], torch.float32, "v_scale"),
+        _dev(out, torch.bfloat16, "out"), B, H, Lq, Lkv, D, int(bool(causal)),
+        float(sm_scale) if sm_scale else 0.0, _stream(stream))
+    check("sage_attn_fwd_prepped", st)
+    return out
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, sm_scale: float = None,
+             out: torch.Tensor = None, workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """sage_attn_fwd: preparation and main loop. workspace (uint8, optional)
+    is reused when large enough."""
+    B, H, Lq, Lkv, D = _dims(q, k)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must match k")
+    nbytes = workspace_bytes(B, H, Lq, Lkv, D)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, Lq, D), dtype=torch.bfloat16, device=q.device)
+    st = lib().sage_attn_fwd(_dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
+                             _dev(v, torch.bfloat16, "v"), _dev(out, torch.bfloat16, "out"), B, H, Lq,
+                             Lkv, D, int(bool(causal)), float(sm_scale) if sm_scale else 0.0,
+                             _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    check("sage_attn_fwd", st)
+    return out
+
+
+def debug_qk_int32(prep: dict, tiles, stream=None) -> torch.Tensor:
+    """sage_debug_qk_int32: int32 [n, 64, 64] QK tiles for (b, h, qb, kb) records."""
+    B, H, Lq, Lkv, D = prep["shape"]
+    arr = (ctypes.c_int * (4 * len(tiles)))(*[int(x) for t in tiles for x in t])
+    acc = torch.empty((max(len(tiles), 1), SAGE_BLOCK, SAGE_BLOCK), dtype=torch.int32,
+                      device=prep["q_i8"].device)
+    st = lib().sage_debug_qk_int32(_dev(prep["q_i8"], torch.int8, "q_i8"), _dev(prep["k_i8"], torch.int8, "k_i8"),
+                                   B, H, Lq, Lkv, D, ctypes.cast(arr, ctypes.c_void_p), len(tiles),
+                                   acc.data_ptr(), _stream(stream))
+    check("sage_debug_qk_int32", st)
+    return acc[:len(tiles)]
+
+
+def debug_codecs(x: torch.Tensor, stream=None):
+    """sage_debug_codecs: (E4M3FN codes, bf16 bits as int16) of fp32 values."""
+    n = x.numel()
+    p8 = torch.empty(n, dtype=torch.uint8, device=x.device)
+    bf = torch.empty(n, dtype=torch.int16, device=x.device)
+    st = lib().sage_debug_codecs(_dev(x, torch.float32, "x"), n, p8.data_ptr(), bf.data_ptr(), _stream(stream))
+    check("sage_debug_codecs", st)
+    return p8, bf
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

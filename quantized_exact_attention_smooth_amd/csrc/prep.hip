@@ -1,0 +1,237 @@
+// Preparation pass on gfx950: K channel mean, K smoothing, INT8 block codes
+// of Q and K, per-channel E4M3FN codes of V.
+//
+// Experiment Log (vortex_exact_attention), "Phase 0 Import And Verification":
+// the imported contract starts with Q/K preparation, K smoothing, INT8
+// quantization and FP8 V. The pass is bound by HBM bandwidth; three launches:
+//   stats    - one read of K and V: per (head, 256-row split) fp64 channel sums
+//              of K and fp32 channel absmax of V (16-byte coalesced loads);
+//   finalize - per head: mean = fp32(sum / Lkv), sv = absmax / 448;
+//   quant    - one read of Q, K, V per 64-row block: block absmax, codes.
+// Every value is bit-identical to the definitions in sage_attn.h: the fp64
+// channel sum of bf16 inputs is exact (the sum of any subset is representable),
+// so the split order does not matter; divisions are IEEE fp32/fp64.
+#include "sage_device.h"
+#include "sage_launch.h"
+
+namespace sage {
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prep_stats_kernel(const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v, int Lkv,
+                                                              int n_split, double* __restrict__ psum,
+                                                              float* __restrict__ pmax) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerIter = kThreads / kLanesPerRow;
+  __shared__ double s_sum[kRowsPerIter][D];
+  __shared__ float s_max[kRowsPerIter][D];
+
+  const int split = blockIdx.x;
+  const long bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int cg = tid % kLanesPerRow, rg = tid / kLanesPerRow;
+  const int t0 = split * kStatRows;
+  const int t1 = min(t0 + kStatRows, Lkv);
+  const uint16_t* kh = k + bh * (long)Lkv * D;
+  const uint16_t* vh = v + bh * (long)Lkv * D;
+
+  double s[8];
+  float mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { s[i] = 0.0; mx[i] = 0.0f; }
+  for (int t = t0 + rg; t < t1; t += kRowsPerIter) {
+    uint4 uk = *reinterpret_cast<const uint4*>(kh + (long)t * D + 8 * cg);
+    uint4 uv = *reinterpret_cast<const uint4*>(vh + (long)t * D + 8 * cg);
+    float fk[8], fv[8];
+    unpack8(uk, fk);
+    unpack8(uv, fv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s[i] += (double)fk[i];
+      mx[i] = fmaxf(mx[i], fabsf(fv[i]));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s_sum[rg][8 * cg + i] = s[i];
+    s_max[rg][8 * cg + i] = mx[i];
+  }
+  __syncthreads();
+  if (tid < D) {
+    double a = 0.0;
+    float m = 0.0f;
+    for (int r = 0; r < kRowsPerIter; ++r) {
+      a += s_sum[r][tid];
+      m = fmaxf(m, s_max[r][tid]);
+    }
+    psum[(bh * n_split + split) * D + tid] = a;
+    pmax[(bh * n_split + split) * D + tid] = m;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void prep_finalize_kernel(const double* __restrict__ psum,
+                                                          const float* __restrict__ pmax, int n_split,
+                                                          int Lkv, float* __restrict__ k_mean,
+                                                          float* __restrict__ v_scale) {
+  const long bh = blockIdx.x;
+  const int c = threadIdx.x;
+  double a = 0.0;
+  float m = 0.0f;
+  for (int s = 0; s < n_split; ++s) {
+    a += psum[(bh * n_split + s) * D + c];
+    m = fmaxf(m, pmax[(bh * n_split + s) * D + c]);
+  }
+  k_mean[bh * D + c] = (float)(a / (double)Lkv);
+  v_scale[bh * D + c] = m / 448.0f;
+}
+
+// Max over the workgroup of one float per thread (all threads get it).
+__device__ __forceinline__ float block_max(float x, float* s_red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) s_red[w] = x;
+  __syncthreads();
+  x = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  return x;
+}
+
+// INT8 codes of one 64-row block of a [L][D] bf16 head (rows >= L are
+// padding: excluded from the absmax and coded 0). sub[c] is subtracted from
+// column c first (the K channel mean; nullptr for Q).
+template <int D>
+__device__ void quant_int8_block(const uint16_t* __restrict__ x, int L, int blk,
+                                 const float* __restrict__ sub, int8_t* __restrict__ codes,
+                                 float* __restrict__ scale, float* s_red) {
+  constexpr int kChunks = kBlock * D / 8 / kThreads;  // 8 values per chunk
+  constexpr int kLanesPerRow = D / 8;
+  float f[kChunks][8];
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int g = threadIdx.x + kThreads * j;
+    const int row = blk * kBlock + g / kLanesPerRow, c0 = 8 * (g % kLanesPerRow);
+    if (row < L) {
+      uint4 u = *reinterpret_cast<const uint4*>(x + (long)row * D + c0);
+      unpack8(u, f[j]);
+      if (sub) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[j][i] = f[j][i] - sub[c0 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[j][i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[j][i] = 0.0f;
+    }
+  }
+  a = block_max(a, s_red);
+  const float s = a / 127.0f;
+  if (threadIdx.x == 0) *scale = s;
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int g = threadIdx.x + kThreads * j;
+    const int row = blk * kBlock + g / kLanesPerRow, c0 = 8 * (g % kLanesPerRow);
+    uint32_t lo = 0, hi = 0;
+    if (row < L) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= ((uint32_t)int8_code(f[j][i], s, a) & 0xFFu) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= ((uint32_t)int8_code(f[j][4 + i], s, a) & 0xFFu) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(codes + (long)(blk * kBlock) * D + (long)(g / kLanesPerRow) * D + c0) =
+        make_uint2(lo, hi);
+  }
+}
+
+// E4M3FN codes of one 64-key block of V, written as a [D][64] tile (keys of a
+// channel contiguous). Each work unit codes 4 consecutive keys x 8 channels,
+// so every LDS write is a whole dword of one channel row.
+template <int D>
+__device__ void quant_v_block(const uint16_t* __restrict__ v, int L, int blk,
+                              const float* __restrict__ sv, uint8_t* __restrict__ tile,
+                              uint8_t* s_tile) {
+  constexpr int kUnits = (kBlock / 4) * (D / 8);
+  for (int u = threadIdx.x; u < kUnits; u += kThreads) {
+    const int kq = u % (kBlock / 4), c0 = 8 * (u / (kBlock / 4));
+    uint32_t packed[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[i] = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = blk * kBlock + 4 * kq + r;
+      if (row < L) {
+        float f[8];
+        unpack8(*reinterpret_cast<const uint4*>(v + (long)row * D + c0), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float s = sv[c0 + i];
+          const uint32_t code = (s != 0.0f) ? e4m3_encode_rne(f[i] / s) : 0u;
+          packed[i] |= code << (8 * r);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint32_t*>(s_tile + (c0 + i) * kBlock + 4 * kq) = packed[i];
+  }
+  __syncthreads();
+  constexpr int kOut = D * kBlock / 16 / kThreads;
+#pragma unroll
+  for (int j = 0; j < kOut; ++j) {
+    const int g = threadIdx.x + kThreads * j;
+    *reinterpret_cast<uint4*>(tile + 16 * g) = *reinterpret_cast<const uint4*>(s_tile + 16 * g);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
+  __shared__ float s_red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[D * kBlock];
+  __shared__ float s_mean[D];
+  __shared__ float s_sv[D];
+  const int blk = blockIdx.x;
+  const long bh = blockIdx.y;
+  if (threadIdx.x < D) {
+    s_mean[threadIdx.x] = a.k_mean[bh * D + threadIdx.x];
+    s_sv[threadIdx.x] = a.v_scale[bh * D + threadIdx.x];
+  }
+  __syncthreads();
+  if (blk < a.nqb)
+    quant_int8_block<D>(a.q + bh * (long)a.Lq * D, a.Lq, blk, nullptr,
+                        a.q_i8 + bh * (long)a.nqb * kBlock * D, a.q_scale + bh * a.nqb + blk, s_red);
+  if (blk < a.nkb) {
+    quant_int8_block<D>(a.k + bh * (long)a.Lkv * D, a.Lkv, blk, s_mean,
+                        a.k_i8 + bh * (long)a.nkb * kBlock * D, a.k_scale + bh * a.nkb + blk, s_red);
+    quant_v_block<D>(a.v + bh * (long)a.Lkv * D, a.Lkv, blk, s_sv,
+                     a.v_fp8 + (bh * a.nkb + blk) * (long)D * kBlock, s_tile);
+  }
+}
+
+int prep_n_split(int Lkv) { return (Lkv + kStatRows - 1) / kStatRows; }
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
+  const int BH = a.B * a.H;
+  const int ns = prep_n_split(a.Lkv);
+  const dim3 g_stats(ns, BH), g_fin(BH), g_quant(a.nqb > a.nkb ? a.nqb : a.nkb, BH);
+  if (a.D == 128) {
+    prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prep_finalize_kernel<128><<<g_fin, 128, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    prep_quant_kernel<128><<<g_quant, kThreads, 0, stream>>>(a);
+  } else {
+    prep_stats_kernel<64><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prep_finalize_kernel<64><<<g_fin, 64, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    prep_quant_kernel<64><<<g_quant, kThreads, 0, stream>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sage

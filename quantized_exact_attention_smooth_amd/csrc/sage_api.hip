@@ -1,0 +1,196 @@
+// C ABI of the quantized attention library: argument validation, workspace
+// layout and kernel launches. Declarations and contracts: include/sage_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "sage_attn.h"
+#include "sage_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
+
+int check_dims(int B, int H, int Lq, int Lkv, int D) {
+  if (B < 1 || H < 1 || Lq < 1 || Lkv < 1) return SAGE_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return SAGE_ERR_UNSUPPORTED;
+  const double elems = (double)B * H * (double)(Lq > Lkv ? Lq : Lkv) * D;
+  if (elems >= 1099511627776.0) return SAGE_ERR_INVALID_ARG;  // 2^40
+  const double qtiles = (double)B * H * ((Lq + sage::kQTile - 1) / sage::kQTile);
+  if (qtiles >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
+struct Layout {
+  size_t q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale, psum, pmax, total;
+};
+
+Layout layout(int B, int H, int Lq, int Lkv, int D) {
+  const size_t bh = (size_t)B * H;
+  const size_t nqb = (Lq + sage::kBlock - 1) / sage::kBlock, nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
+  const size_t ns = sage::prep_n_split(Lkv);
+  Layout l;
+  size_t o = 0;
+  l.q_i8 = o;    o = align_up(o + bh * nqb * sage::kBlock * D);
+  l.q_scale = o; o = align_up(o + bh * nqb * sizeof(float));
+  l.k_i8 = o;    o = align_up(o + bh * nkb * sage::kBlock * D);
+  l.k_scale = o; o = align_up(o + bh * nkb * sizeof(float));
+  l.k_mean = o;  o = align_up(o + bh * D * sizeof(float));
+  l.v_fp8 = o;   o = align_up(o + bh * nkb * sage::kBlock * D);
+  l.v_scale = o; o = align_up(o + bh * D * sizeof(float));
+  l.psum = o;    o = align_up(o + bh * ns * D * sizeof(double));
+  l.pmax = o;    o = align_up(o + bh * ns * D * sizeof(float));
+  l.total = o;
+  return l;
+}
+
+size_t prep_scratch(int B, int H, int Lkv, int D) {
+  const size_t n = (size_t)B * H * sage::prep_n_split(Lkv) * D;
+  return align_up(n * sizeof(double)) + align_up(n * sizeof(float));
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_status_str(int status) {
+  switch (status) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_INVALID_ARG: return "SAGE_ERR_INVALID_ARG";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED";
+    case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE";
+    case SAGE_ERR_HIP: return "SAGE_ERR_HIP";
+    default: return "SAGE_ERR_UNKNOWN";
+  }
+}
+
+int sage_prep_scratch_bytes(int B, int H, int Lq, int Lkv, int D, size_t* bytes) {
+  if (!bytes) return SAGE_ERR_INVALID_ARG;
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  *bytes = prep_scratch(B, H, Lkv, D);
+  return SAGE_OK;
+}
+
+int sage_workspace_bytes(int B, int H, int Lq, int Lkv, int D, size_t* bytes) {
+  if (!bytes) return SAGE_ERR_INVALID_ARG;
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  *bytes = layout(B, H, Lq, Lkv, D).total;
+  return SAGE_OK;
+}
+
+int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
+                    int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                    uint8_t* v_fp8, float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  if (!q || !k || !v || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !v_fp8 || !v_scale || !scratch)
+    return SAGE_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(q_i8, 16) ||
+      misaligned(k_i8, 16) || misaligned(v_fp8, 16) || misaligned(q_scale, 4) || misaligned(k_scale, 4) ||
+      misaligned(k_mean, 16) || misaligned(v_scale, 16) || misaligned(scratch, 8))
+    return SAGE_ERR_INVALID_ARG;
+  if (scratch_bytes < prep_scratch(B, H, Lkv, D)) return SAGE_ERR_WORKSPACE;
+  const size_t n = (size_t)B * H * sage::prep_n_split(Lkv) * D;
+  sage::PrepArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.B = B; a.H = H; a.Lq = Lq; a.Lkv = Lkv; a.D = D;
+  a.nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
+  a.nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
+  a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale; a.k_mean = k_mean;
+  a.v_fp8 = v_fp8; a.v_scale = v_scale;
+  a.psum = (double*)scratch;
+  a.pmax = (float*)((char*)scratch + align_up(n * sizeof(double)));
+  return hip_status(sage::launch_prep(a, (hipStream_t)stream));
+}
+
+int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                          const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
+                          int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, void* stream) {
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_fp8 || !v_scale || !out) return SAGE_ERR_INVALID_ARG;
+  if (misaligned(q_i8, 16) || misaligned(k_i8, 16) || misaligned(v_fp8, 16) || misaligned(out, 16) ||
+      misaligned(q_scale, 4) || misaligned(k_scale, 4) || misaligned(v_scale, 16))
+    return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (isnan(sm_scale) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
+  if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
+  sage::AttnArgs a;
+  a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale;
+  a.v_fp8 = v_fp8; a.v_scale = v_scale; a.out = (uint16_t*)out;
+  a.B = B; a.H = H; a.Lq = Lq; a.Lkv = Lkv;
+  a.nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
+  a.nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
+  a.n_qtiles = (Lq + sage::kQTile - 1) / sage::kQTile;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  return hip_status(sage::launch_attn(a, D, causal == 1, (hipStream_t)stream));
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
+                  int D, int causal, float sm_scale, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  if (!q || !k || !v || !out || !workspace) return SAGE_ERR_INVALID_ARG;
+  if (misaligned(workspace, kAlign) || misaligned(out, 16)) return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (isnan(sm_scale) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
+  const Layout l = layout(B, H, Lq, Lkv, D);
+  if (workspace_bytes < l.total) return SAGE_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  int s = sage_quant_prep(q, k, v, B, H, Lq, Lkv, D, (int8_t*)(ws + l.q_i8), (float*)(ws + l.q_scale),
+                          (int8_t*)(ws + l.k_i8), (float*)(ws + l.k_scale), (float*)(ws + l.k_mean),
+                          (uint8_t*)(ws + l.v_fp8), (float*)(ws + l.v_scale), ws + l.psum,
+                          l.total - l.psum, stream);
+  if (s != SAGE_OK) return s;
+  return sage_attn_fwd_prepped((const int8_t*)(ws + l.q_i8), (const float*)(ws + l.q_scale),
+                               (const int8_t*)(ws + l.k_i8), (const float*)(ws + l.k_scale),
+                               (const uint8_t*)(ws + l.v_fp8), (const float*)(ws + l.v_scale), out, B, H, Lq,
+                               Lkv, D, causal, sm_scale, stream);
+}
+
+int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int Lq, int Lkv, int D,
+                        const int* tiles, int n_tiles, int32_t* acc_out, void* stream) {
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  if (!q_i8 || !k_i8 || !tiles || !acc_out || n_tiles < 0) return SAGE_ERR_INVALID_ARG;
+  if (misaligned(q_i8, 16) || misaligned(k_i8, 16) || misaligned(acc_out, 16)) return SAGE_ERR_INVALID_ARG;
+  sage::QkDebugArgs a;
+  a.q_i8 = q_i8; a.k_i8 = k_i8;
+  a.Lq = Lq; a.Lkv = Lkv; a.H = H;
+  a.nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
+  a.nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
+  for (int i = 0; i < n_tiles; ++i) {
+    const int* t = tiles + 4 * i;
+    if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= H || t[2] < 0 || t[2] >= a.nqb || t[3] < 0 ||
+        t[3] >= a.nkb)
+      return SAGE_ERR_INVALID_ARG;
+  }
+  for (int base = 0; base < n_tiles; base += sage::kMaxDebugTiles) {
+    a.n = n_tiles - base < sage::kMaxDebugTiles ? n_tiles - base : sage::kMaxDebugTiles;
+    for (int i = 0; i < a.n; ++i)
+      for (int j = 0; j < 4; ++j) a.tiles[i][j] = tiles[4 * (base + i) + j];
+    a.acc_out = acc_out + (size_t)base * sage::kBlock * sage::kBlock;
+    const int s = hip_status(sage::launch_qk_debug(a, D, (hipStream_t)stream));
+    if (s != SAGE_OK) return s;
+  }
+  return SAGE_OK;
+}
+
+int sage_debug_codecs(const float* x, int n, uint8_t* p8, uint16_t* bf16, void* stream) {
+  if (!x || !p8 || !bf16 || n < 0) return SAGE_ERR_INVALID_ARG;
+  if (misaligned(x, 4) || misaligned(bf16, 2)) return SAGE_ERR_INVALID_ARG;
+  if (n == 0) return SAGE_OK;
+  return hip_status(sage::launch_codecs_debug(x, n, p8, bf16, (hipStream_t)stream));
+}
+
+}  // extern "C"

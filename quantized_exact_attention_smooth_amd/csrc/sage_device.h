@@ -1,0 +1,83 @@
+// Device helpers of the gfx950 quantized-attention kernels (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sage_launch.h"
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Eight bf16 values from one 16-byte word.
+__device__ __forceinline__ void unpack8(const uint4& u, float f[8]) {
+  f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x);
+  f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+  f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z);
+  f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+}
+
+// INT8 block code: fp32 quotient (IEEE division) rounded half-to-even,
+// clamped to [-127, 127]; an all-zero block (a == 0) codes to 0.
+__device__ __forceinline__ int int8_code(float x, float s, float a) {
+  if (a == 0.0f) return 0;
+  float r = rintf(x / s);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+// fp32 -> OCP E4M3FN, round to nearest even, saturating to +-448, zero keeps
+// the sign. Normal range: keep 3 of the 23 fraction bits with round-half-even
+// on the 20 dropped bits. Below 2^-6 the code is the nearest multiple of 2^-9
+// (x * 2^9 is exact), which also yields the smallest normal (code 8) when the
+// value rounds up to 2^-6.
+__device__ __forceinline__ uint32_t e4m3_encode_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (!(a < 448.0f)) return (a != a) ? 0x7Fu : (sign | 0x7Eu);
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+  uint32_t ua = __float_as_uint(a);
+  uint32_t e = ((ua >> 23) & 0xFFu) - 127u + 7u;  // 1..15
+  uint32_t frac = ua & 0x7FFFFFu;
+  uint32_t m = frac >> 20, rem = frac & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) {
+    m += 1u;
+    if (m == 8u) { m = 0u; e += 1u; }
+  }
+  uint32_t code = (e << 3) | m;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+// Byte offset of 16-byte chunk `chunk` of key row `key` in an LDS K tile of
+// 64 rows x D bytes. The XOR keeps the eight keys one A-operand read
+// instruction touches per group of eight lanes on distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_lds_off(int key, int chunk) {
+  int swz = (D == 128) ? ((key ^ (key >> 3)) & 7) : (((key >> 1) & 1) | ((key >> 4) & 2));
+  return key * D + ((chunk ^ swz) << 4);
+}
+
+// Byte offset of 16-byte chunk `chunk` (0..3) of channel row `c` in an LDS V
+// tile of D rows x 64 key bytes.
+__device__ __forceinline__ int v_lds_off(int c, int chunk) {
+  return c * 64 + ((chunk ^ ((c >> 1) & 3)) << 4);
+}
+
+// A-operand row -> key mapping of the QK matrix-core step. The 32x32 int32
+// result gives lane (h = lane/32, q = lane%32), register r the row
+// 8*(r/4) + 4*h + (r%4). Loading key 32*h + 16*m + 4*(row/8) + (row%4) for
+// row = 8*(row/8) + 4*h + (row%4) makes register r of half h hold key
+// 32*h + 16*m + r: each lane ends with 32 consecutive keys of one query.
+__device__ __forceinline__ int qk_row_key(int row, int m) {
+  return 32 * ((row >> 2) & 1) + 16 * m + 4 * (row >> 3) + (row & 3);
+}
+
+}  // namespace sage

@@ -1,0 +1,57 @@
+// Kernel argument blocks and launchers of the HIP library (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+constexpr int kBlock = 64;      // quant block rows == attention epoch keys
+constexpr int kThreads = 256;   // 4 wave64 per workgroup
+constexpr int kQTile = 128;     // query rows per main-loop workgroup (32 per wave)
+constexpr int kStatRows = 256;  // key rows per preparation statistics workgroup
+
+struct PrepArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int B, H, Lq, Lkv, D, nqb, nkb;
+  int8_t* q_i8;
+  float* q_scale;
+  int8_t* k_i8;
+  float* k_scale;
+  float* k_mean;
+  uint8_t* v_fp8;
+  float* v_scale;
+  double* psum;  // [B*H][n_split][D] fp64 channel partial sums of K
+  float* pmax;   // [B*H][n_split][D] channel absmax partials of V
+};
+
+struct AttnArgs {
+  const int8_t* q_i8;
+  const float* q_scale;
+  const int8_t* k_i8;
+  const float* k_scale;
+  const uint8_t* v_fp8;
+  const float* v_scale;
+  uint16_t* out;
+  int B, H, Lq, Lkv, nqb, nkb, n_qtiles;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+constexpr int kMaxDebugTiles = 64;
+struct QkDebugArgs {
+  const int8_t* q_i8;
+  const int8_t* k_i8;
+  int32_t* acc_out;
+  int Lq, Lkv, nqb, nkb, H, n;
+  int tiles[kMaxDebugTiles][4];
+};
+
+int prep_n_split(int Lkv);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream);
+hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream);
+hipError_t launch_codecs_debug(const float* x, int n, uint8_t* p8, uint16_t* bf16, hipStream_t stream);
+
+}  // namespace sage

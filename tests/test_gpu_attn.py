@@ -1,0 +1,166 @@
+"""The fused main loop and the whole path against the oracle.
+
+Bar: per checked head or block, max-abs <= 2e-2 and mean-abs <= 2e-3 of the
+bf16 output against the oracle's bf16 output from the same bf16 inputs
+(P bytes, exp and summation order differ between the two, so outputs are
+not expected to be bit-identical). Exact expectations where the math fixes
+the result (zero Q with constant V, one-hot keys). Full-size workloads run
+in the same launch configuration the benchmark times and are checked on
+their seeded oracle subsets.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+import quantized_exact_attention_smooth_amd as sage
+from _parity import assert_out_close, oracle_preps, oracle_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_out(q, k, v, causal, sm_scale, dev, end_to_end=False):
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    if end_to_end:
+        o = sage.attn_fwd(qg, kg, vg, causal, sm_scale)
+    else:
+        o = sage.attn_fwd_prepped(sage.quant_prep(qg, kg, vg), causal, sm_scale)
+    torch.cuda.synchronize()
+    return si.bf16_bits(o)
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_small_workloads_all_rows(idx, gpu_device):
+    w = si.WORKLOADS[idx]
+    say(f"attn parity (all rows): {w.name}")
+    q, k, v = si.workload_qkv(w)
+    out = _gpu_out(q, k, v, w.causal, w.sm_scale, gpu_device)
+    for (b, h), o in oracle_preps(q, k, v, si.oracle_heads(w)).items():
+        ref = oracle_rows(o, w.causal, w.sm_scale, 0, w.Lq)
+        assert_out_close(out[b, h], ref, f"{w.name} head {(b, h)}")
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_full_size_workloads_on_oracle_subset(idx, gpu_device):
+    w = si.WORKLOADS[idx]
+    say(f"attn parity (oracle subset): {w.name}")
+    q, k, v = si.workload_qkv(w)
+    out = _gpu_out(q, k, v, w.causal, w.sm_scale, gpu_device)
+    if w.oracle_subset[0] == "blocks":
+        items = [(b, h, qb * 64, min(w.Lq, qb * 64 + 64)) for (b, h, qb) in si.oracle_blocks(w)]
+    else:
+        items = [(b, h, 0, w.Lq) for (b, h) in si.oracle_heads(w)]
+    preps = oracle_preps(q, k, v, sorted({(b, h) for (b, h, _, _) in items}))
+    worst = (0.0, 0.0)
+    for (b, h, r0, r1) in items:
+        ref = oracle_rows(preps[(b, h)], w.causal, w.sm_scale, r0, r1)
+        mx, mean = assert_out_close(out[b, h, r0:r1], ref, f"{w.name} {(b, h, r0, r1)}")
+        worst = (max(worst[0], mx), max(worst[1], mean))
+    say(f"  worst max-abs {worst[0]:.3e} mean-abs {worst[1]:.3e}")
+
+
+SHAPES = [(1, 1, 1, 1, 64, False), (1, 1, 1, 1, 128, True), (1, 2, 63, 63, 64, True), (1, 1, 64, 64, 128, False),
+          (1, 1, 65, 65, 128, True), (1, 2, 127, 129, 64, False), (1, 1, 129, 127, 128, True),
+          (2, 3, 200, 333, 128, True), (1, 1, 1000, 64, 64, True), (1, 1, 64, 1000, 128, True),
+          (1, 1, 191, 193, 64, False), (1, 2, 300, 300, 128, True), (1, 1, 257, 1, 128, False),
+          (1, 1, 384, 384, 64, True)]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lkv,D,causal", SHAPES)
+def test_ragged_and_edge_shapes(B, H, Lq, Lkv, D, causal, gpu_device):
+    say(f"attn parity: shape {(B, H, Lq, Lkv, D, causal)}")
+    q, k, v = si.make_qkv(B, H, Lq, Lkv, D, "normal", 2.0, seed=Lq * 5 + Lkv + D)
+    sc = 1 / math.sqrt(D)
+    out = _gpu_out(q, k, v, causal, sc, gpu_device)
+    for (b, h), o in oracle_preps(q, k, v, [(b, h) for b in range(B) for h in range(H)]).items():
+        ref = oracle_rows(o, causal, sc, 0, Lq)
+        assert_out_close(out[b, h], ref, f"head {(b, h)}")
+        if causal and Lq > Lkv:
+            assert np.all(out[b, h, :Lq - Lkv] == 0)
+
+
+def test_end_to_end_equals_prep_then_main(gpu_device):
+    w = si.WORKLOADS[1]
+    q, k, v = si.workload_qkv(w)
+    say("attn_fwd == quant_prep + attn_fwd_prepped")
+    a = _gpu_out(q, k, v, True, w.sm_scale, gpu_device, end_to_end=True)
+    b = _gpu_out(q, k, v, True, w.sm_scale, gpu_device)
+    assert np.array_equal(a, b)
+
+
+def test_default_scale_is_one_over_sqrt_d(gpu_device):
+    q, k, v = si.make_qkv(1, 2, 150, 150, 64, "normal", 1.0, seed=9)
+    say("sm_scale <= 0 selects 1/sqrt(D)")
+    a = _gpu_out(q, k, v, True, 0.0, gpu_device)
+    b = _gpu_out(q, k, v, True, 0.125, gpu_device)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("L,D,causal", [(192, 128, False), (300, 64, True), (1000, 128, True)])
+def test_zero_q_constant_v_is_exact(L, D, causal, gpu_device):
+    _, k, _ = si.make_qkv(1, 1, L, L, D, "normal", 2.0, seed=L)
+    vc = torch.from_numpy(np.random.default_rng(L).normal(0, 2, D).astype(np.float32)).to(torch.bfloat16)
+    v = vc.reshape(1, 1, 1, D).expand(1, 1, L, D).contiguous()
+    q = torch.zeros((1, 1, L, D), dtype=torch.bfloat16)
+    say(f"zero Q, constant V: {(L, D, causal)}")
+    out = _gpu_out(q, k, v, causal, 1 / math.sqrt(D), gpu_device)
+    want = np.broadcast_to(si.bf16_bits(vc), (L, D))
+    assert np.array_equal(out[0, 0], want)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_hot_keys_exact(D, causal, gpu_device):
+    L = D
+    rng = np.random.default_rng(D + causal)
+    perm = rng.permutation(D)
+    qk = np.zeros((L, D), np.float32)
+    qk[np.arange(L), perm] = 16.0
+    vv = (rng.uniform(0.5, 1.0, (L, D)) * rng.choice([-1, 1], (L, D))).astype(np.float32)
+    vv[0, :] = 1.0
+    t = lambda x: torch.from_numpy(x).to(torch.bfloat16).reshape(1, 1, L, D)
+    say(f"one-hot keys: D={D} causal={causal}")
+    out = _gpu_out(t(qk), t(qk), t(vv), causal, 1 / math.sqrt(D), gpu_device)
+    p = oracle.prep_head(si.bf16_bits(t(qk))[0, 0], si.bf16_bits(t(qk))[0, 0], si.bf16_bits(t(vv))[0, 0])
+    dec = oracle.e4m3_decode(p["v8"][:L]).astype(np.float32)
+    want = oracle.bf16_round(dec * p["v_scale"][None, :])
+    assert np.array_equal(out[0, 0], want)
+
+
+def test_repeated_launches_are_bit_identical(gpu_device):
+    """Fixed reduction order and no atomics in the main loop: 1000 launches
+    of the 128x192 workload and 50 of the ragged causal one repeat exactly."""
+    for idx, reps in ((0, 1000), (1, 50)):
+        w = si.WORKLOADS[idx]
+        q, k, v = (t.to(gpu_device) for t in si.workload_qkv(w))
+        p = sage.quant_prep(q, k, v)
+        first = sage.attn_fwd_prepped(p, w.causal, w.sm_scale).clone()
+        say(f"repetition x{reps}: {w.name}")
+        outs = torch.empty((reps,) + tuple(first.shape), dtype=first.dtype, device=gpu_device) if reps <= 64 else None
+        for i in range(reps):
+            o = sage.attn_fwd_prepped(p, w.causal, w.sm_scale)
+            if outs is not None:
+                outs[i] = o
+            else:
+                assert torch.equal(o.view(torch.int16), first.view(torch.int16)), i
+        if outs is not None:
+            assert torch.equal(outs.view(torch.int16), first.view(torch.int16).expand_as(outs))
+        torch.cuda.synchronize()
+
+
+def test_oracle_accuracy_holds_for_gpu_output(gpu_device):
+    """GPU output against brute-force fp64 attention: cosine >= 0.995 on the
+    ragged causal workload (all heads)."""
+    w = si.WORKLOADS[1]
+    q, k, v = si.workload_qkv(w)
+    say("gpu vs fp64 cosine")
+    out = _gpu_out(q, k, v, w.causal, w.sm_scale, gpu_device)
+    for h in range(w.H):
+        qf, kf, vf = (oracle.bf16_to_f32(si.bf16_bits(t[0, h])).astype(np.float64) for t in (q, k, v))
+        ref = oracle.attn_ref_parallel(qf, kf, vf, w.causal, w.sm_scale)
+        a = oracle.bf16_to_f32(out[0, h]).astype(np.float64).ravel()
+        cos = a @ ref.ravel() / math.sqrt((a @ a) * (ref.ravel() @ ref.ravel()))
+        assert cos >= 0.995, (h, cos)
