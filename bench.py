@@ -72,6 +72,24 @@ def cpu_baseline(w) -> dict:
                       f"{dt:.2f} s wall on {threads} threads"}
 
 
+def copy_calibration(nbytes: int, steps: int) -> int:
+    """A plain device-to-device copy of known size: its FETCH_SIZE and
+    WRITE_SIZE counter readings scale the main kernel's readings to bytes."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes": x.numel() * 4, "ms": dt * 1e3, "GBps_each_way": x.numel() * 4 / dt / 1e9}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,6 +97,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=None, help="index into seeded_inputs.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="calibration only: time a plain device copy of this many bytes and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -89,6 +109,9 @@ def main() -> int:
     import torch
     import seeded_inputs as si
     from quantized_exact_attention_smooth_amd import _lib
+
+    if args.copy_bytes:
+        return copy_calibration(args.copy_bytes, args.steps)
 
     w = si.WORKLOADS[si.HEADLINE if args.workload is None else args.workload]
     dev = torch.device("cuda:0")

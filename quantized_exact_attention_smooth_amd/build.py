@@ -16,8 +16,11 @@ LIB = os.path.join(PKG, "libsage_attn.so")
 SOURCES = ["prep.hip", "attn_fwd.hip", "sage_api.hip"]
 
 # -packed-fp32-ops off: no packed fp32 VALU instructions are generated.
+# -amdgpu-mfma-vgpr-form: matrix-core results land in VGPRs, which the
+# softmax and RO update read directly (no AGPR-to-VGPR copies).
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form",
                "-I", INCLUDE, "-I", CSRC]
 
 

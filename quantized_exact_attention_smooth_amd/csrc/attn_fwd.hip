@@ -30,6 +30,8 @@
 //  * epilogue: r = 1/l (IEEE divide), out = bf16(RO * r * sv[c]) for rows < Lq.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "sage_device.h"
 #include "sage_launch.h"
 
@@ -108,17 +110,73 @@ __device__ __forceinline__ uint32_t pack2_bf16(float x0, float x1) {
   return (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
 }
 
+// Direct global -> LDS copies (no staging registers). A wave copies 64
+// consecutive 16-byte LDS chunks per instruction; each lane fetches the global
+// chunk that the swizzled layout places at its LDS position.
+template <int D>
+__device__ __forceinline__ void k_tile_to_lds(const int8_t* __restrict__ src, uint8_t* lds, int w, int lane) {
+  constexpr int kPerWave = kBlock * D / 16 / 4 / 64;  // instructions per wave
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int p0 = (w * kPerWave + j) * 64;
+    const int p = p0 + lane;
+    const int key = p / (D / 16), pc = p % (D / 16);
+    const int c = (k_lds_off<D>(key, pc) - key * D) >> 4;  // logical chunk at physical pc
+    __builtin_amdgcn_global_load_lds(src + key * D + 16 * c, lds + 16 * p0, 16, 0, 0);
+  }
+}
+template <int D>
+__device__ __forceinline__ void v_tile_to_lds(const uint8_t* __restrict__ src, uint8_t* lds, int w, int lane) {
+  constexpr int kPerWave = D * kBlock / 16 / 4 / 64;
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int p0 = (w * kPerWave + j) * 64;
+    const int p = p0 + lane;
+    const int row = p / 4, pc = p % 4;
+    const int c = (v_lds_off(row, pc) - row * 64) >> 4;
+    __builtin_amdgcn_global_load_lds(src + row * 64 + 16 * c, lds + 16 * p0, 16, 0, 0);
+  }
+}
+
+// Pairwise exchange between lane halves: returns f(own, other) in every lane.
+// v_permlane32_swap with the same value in both operands leaves, per lane,
+// its own value in one result and the other half's value in the other.
+__device__ __forceinline__ int half_max(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 // ------------------------------------------------------------ main kernel
+//
+// Software pipeline per wave, one body per epoch e:
+//   1. start the LDS fills of K(e+2) and V(e+1) (buffers freed by the last
+//      barrier);
+//   2. QK matrix-core steps for epoch e+1 into the other accumulator set;
+//   3. softmax of epoch e (VALU) from the accumulators filled one body ago;
+//   4. RO *= alpha when some row's running max moved, then the PV step of
+//      epoch e accumulates into RO inside the matrix core;
+//   5. wait for this body's LDS fills, barrier.
+// The QK results of step 2 and the PV results of step 4 are consumed one body
+// later, so neither matrix-core latency is exposed to the softmax.
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kBlock * D];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][D * kBlock];
+  // Four separate LDS objects (not one array) so that the compiler can tell
+  // the in-flight direct fills apart from the buffers being read.
+  __shared__ __attribute__((aligned(16))) uint8_t s_k0[kBlock * D];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k1[kBlock * D];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v0[D * kBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v1[D * kBlock];
 
   const int BH = a.B * a.H;
   const int tile = a.n_qtiles - 1 - (int)(blockIdx.x / BH);
   const long bh = blockIdx.x % BH;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int h = lane >> 5, ql = lane & 31;
   const int q0 = tile * kQTile;
   const int wrow0 = q0 + 32 * w;
@@ -137,8 +195,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
     const int x = CAUSAL ? min(a.Lq - 1, wrow0 + 31) + off : a.Lkv - 1;
     w_ep = x < 0 ? 0 : min(a.nkb, x / kBlock + 1);
   }
-  // Keys beyond lim (this lane's last visible key) are masked; an epoch needs
-  // the mask only when it reaches past the wave's smallest limit.
+  // Keys beyond lim (this lane's last visible key) are masked. An epoch needs
+  // the mask only when it reaches past the wave's smallest limit w_lim.
   const int lim = CAUSAL ? min(qrow + off, a.Lkv - 1) : a.Lkv - 1;
   const int w_lim = CAUSAL ? min(wrow0 + off, a.Lkv - 1) : a.Lkv - 1;
 
@@ -151,6 +209,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
                               : v4i{};
   }
   const float sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
+  const float cq = sq * a.scale_log2;
 
   float m = -INFINITY, l = 0.0f;
   v16f ro[D / 32];
@@ -159,86 +218,99 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 
   const int8_t* kh = a.k_i8 + bh * (long)a.nkb * kBlock * D;
   const uint8_t* vh = a.v_fp8 + bh * (long)a.nkb * D * kBlock;
-  const float* ksh = a.k_scale + bh * a.nkb;
-  KStage<D, kThreads> ks;
-  VStage<D, kThreads> vs;
+  // k_scale is read-only for the kernel's lifetime: scalar (constant-space) loads.
+  const __attribute__((address_space(4))) float* ksh =
+      (const __attribute__((address_space(4))) float*)(a.k_scale + bh * a.nkb);
+
+  v16i sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
   if (n_ep > 0) {
-    ks.load(kh);
-    vs.load(vh);
-    ks.store(s_k[0]);
-    vs.store(s_v[0]);
+    k_tile_to_lds<D>(kh, s_k0, w, lane);
+    v_tile_to_lds<D>(vh, s_v0, w, lane);
+    if (n_ep > 1) k_tile_to_lds<D>(kh + kBlock * D, s_k1, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
+  if (w_ep > 0) qk_epoch<D>(s_k0, qreg, lane, sa0, sa1);
 
-  for (int e = 0; e < n_ep; ++e) {
-    const int buf = e & 1;
-    if (e + 1 < n_ep) {
-      ks.load(kh + (long)(e + 1) * kBlock * D);
-      vs.load(vh + (long)(e + 1) * D * kBlock);
-    }
+  // One pipelined epoch: `cur` holds S(e), `nxt` receives S(e+1). The epoch's
+  // parity is a template argument so every LDS buffer is a fixed object.
+  auto body = [&](auto parity, const int e, const v16i& cur0, const v16i& cur1, v16i& nxt0, v16i& nxt1) {
+    constexpr int P = decltype(parity)::value;
+    uint8_t* k_fill = P ? s_k1 : s_k0;   // K(e+2) replaces K(e)
+    uint8_t* k_next = P ? s_k0 : s_k1;   // K(e+1)
+    uint8_t* v_cur = P ? s_v1 : s_v0;    // V(e)
+    uint8_t* v_fill = P ? s_v0 : s_v1;   // V(e+1) replaces V(e-1)
+    if (e + 2 < n_ep) k_tile_to_lds<D>(kh + (long)(e + 2) * kBlock * D, k_fill, w, lane);
+    if (e + 1 < n_ep) v_tile_to_lds<D>(vh + (long)(e + 1) * D * kBlock, v_fill, w, lane);
+    if (e + 1 < w_ep) qk_epoch<D>(k_next, qreg, lane, nxt0, nxt1);
     if (e < w_ep) {
-      v16i acc0, acc1;
-      qk_epoch<D>(s_k[buf], qreg, lane, acc0, acc1);
-
-      const float c = sq * ksh[e] * a.scale_log2;
-      const int kbase = kBlock * e + 32 * h;
-      const bool masked = kBlock * e + kBlock - 1 > w_lim;
+      // log2-domain score per unit of the int32 accumulator
+      const float c = cq * ksh[e];
       int x[32];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        x[r] = acc0[r];
-        x[16 + r] = acc1[r];
+        x[r] = cur0[r];
+        x[16 + r] = cur1[r];
       }
+      const bool masked = kBlock * e + kBlock - 1 > w_lim;  // wave-uniform
+      const int dlim = lim - (kBlock * e + 32 * h);          // x[t] visible iff t <= dlim
       if (masked) {
 #pragma unroll
-        for (int t = 0; t < 32; ++t)
-          if (kbase + t > lim) x[t] = INT_MIN;
+        for (int t = 0; t < 32; ++t) x[t] = (t > dlim) ? INT_MIN : x[t];
       }
-      int mx = x[0];
+      int mx = max(max(x[0], x[1]), x[2]);
 #pragma unroll
-      for (int t = 1; t < 32; ++t) mx = max(mx, x[t]);
-      mx = max(mx, __shfl_xor(mx, 32, 64));
+      for (int t = 3; t < 31; t += 2) mx = max(max(mx, x[t]), x[t + 1]);
+      mx = max(mx, x[31]);
+      mx = half_max(mx);
       const float mt = (kBlock * e <= lim) ? (float)mx * c : -INFINITY;
       const float m_new = fmaxf(m, mt);
       const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;  // wave-uniform
 
       float p[32];
-      float ps = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)x[t], c, -m_use));
-        if (masked && kbase + t > lim) p[t] = 0.0f;
-        ps += p[t];
+      for (int t = 0; t < 32; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)x[t], c, -m_use));
+      if (masked) {
+#pragma unroll
+        for (int t = 0; t < 32; ++t) p[t] = (t > dlim) ? 0.0f : p[t];
       }
-      l = l * alpha + ps;
+      float ps = p[0];
+#pragma unroll
+      for (int t = 1; t < 32; ++t) ps += p[t];
+      l = __builtin_fmaf(l, alpha, ps);
 
       v8i pb;
 #pragma unroll
       for (int d = 0; d < 8; ++d) pb[d] = pack4_fp8(p[4 * d], p[4 * d + 1], p[4 * d + 2], p[4 * d + 3]);
 
-      const uint8_t* lv = s_v[buf];
+      // Per-tile rescale; a no-op (alpha == 1 in every lane) when no row max moved.
+      if (moved) {
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb) ro[cb] *= alpha;
+      }
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb) {
         const int ch = 32 * cb + ql;
-        const v4i lo = *reinterpret_cast<const v4i*>(lv + v_lds_off(ch, 2 * h));
-        const v4i hi = *reinterpret_cast<const v4i*>(lv + v_lds_off(ch, 2 * h + 1));
+        const v4i lo = *reinterpret_cast<const v4i*>(v_cur + v_lds_off(ch, 2 * h));
+        const v4i hi = *reinterpret_cast<const v4i*>(v_cur + v_lds_off(ch, 2 * h + 1));
         const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const v16f pv = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, v16f{}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ro[cb][r] = __builtin_fmaf(ro[cb][r], alpha, pv[r]);
+        ro[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, ro[cb], 0, 0, 0, 127, 0, 127);
       }
       m = m_new;
     }
-    if (e + 1 < n_ep) {
-      ks.store(s_k[buf ^ 1]);
-      vs.store(s_v[buf ^ 1]);
-    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  for (int e = 0; e < n_ep; e += 2) {
+    body(std::integral_constant<int, 0>{}, e, sa0, sa1, sb0, sb1);
+    if (e + 1 < n_ep) body(std::integral_constant<int, 1>{}, e + 1, sb0, sb1, sa0, sa1);
   }
 
-  // Epilogue: both halves of a query hold partial sums of l.
-  const float lt = l + __shfl_xor(l, 32, 64);
+  // Epilogue: the two halves of a query hold partial sums of l.
+  const float lt = half_sum(l);
   const float rcp = (lt > 0.0f) ? 1.0f / lt : 0.0f;
   if (qrow < a.Lq) {
     uint16_t* orow = a.out + (bh * a.Lq + qrow) * (long)D;

@@ -57,18 +57,24 @@ __device__ __forceinline__ uint32_t e4m3_encode_rne(float x) {
 }
 
 // Byte offset of 16-byte chunk `chunk` of key row `key` in an LDS K tile of
-// 64 rows x D bytes. The XOR keeps the eight keys one A-operand read
-// instruction touches per group of eight lanes on distinct 16-byte bank groups.
+// 64 rows x D bytes. The XOR swizzle is linear in the key bits and was chosen
+// so that the A-operand reads of the QK step (16 bytes per lane) and the
+// staging writes touch distinct 16-byte bank groups both per 8 lanes in a
+// 128-byte window and per 16 lanes in a 256-byte window.
 template <int D>
 __device__ __forceinline__ int k_lds_off(int key, int chunk) {
-  int swz = (D == 128) ? ((key ^ (key >> 3)) & 7) : (((key >> 1) & 1) | ((key >> 4) & 2));
+  int swz;
+  if (D == 128)
+    swz = ((key >> 1) & 1) | (((key ^ (key >> 2)) & 1) << 1) | (((key >> 5) & 1) << 2);
+  else
+    swz = (((key >> 1) ^ (key >> 2)) & 1) | (((key >> 5) & 1) << 1);
   return key * D + ((chunk ^ swz) << 4);
 }
 
 // Byte offset of 16-byte chunk `chunk` (0..3) of channel row `c` in an LDS V
-// tile of D rows x 64 key bytes.
+// tile of D rows x 64 key bytes (same two bank-group conditions).
 __device__ __forceinline__ int v_lds_off(int c, int chunk) {
-  return c * 64 + ((chunk ^ ((c >> 1) & 3)) << 4);
+  return c * 64 + ((chunk ^ (((c >> 1) ^ (c >> 2)) & 3)) << 4);
 }
 
 // A-operand row -> key mapping of the QK matrix-core step. The 32x32 int32
