@@ -97,10 +97,22 @@ __device__ __forceinline__ void qk_epoch(const uint8_t* lk, const v4i* qreg, int
   }
 }
 
+// Maximum of one lane's 32 scores (v_max3 chain).
+__device__ __forceinline__ int row_max32(const int (&x)[32]) {
+  int mx = max(max(x[0], x[1]), x[2]);
+#pragma unroll
+  for (int t = 3; t < 31; t += 2) mx = max(max(mx, x[t]), x[t + 1]);
+  return max(mx, x[31]);
+}
+
 // Four fp32 values -> four E4M3FN bytes (x0 in the low byte), hardware
 // conversion, round to nearest even.
 __device__ __forceinline__ int pack4_fp8(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  // Both halves of the word are written, so its prior contents are irrelevant;
+  // an empty asm output stands for them and saves a register clear.
+  int w;
+  asm volatile("" : "=v"(w));
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, w, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
@@ -231,6 +243,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   }
   __syncthreads();
   if (w_ep > 0) qk_epoch<D>(s_k0, qreg, lane, sa0, sa1);
+  // The first epoch refills s_k0 with K(2): every wave must have read K(0) first.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // One pipelined epoch: `cur` holds S(e), `nxt` receives S(e+1). The epoch's
   // parity is a template argument so every LDS buffer is a fixed object.
@@ -254,14 +269,18 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
       }
       const bool masked = kBlock * e + kBlock - 1 > w_lim;  // wave-uniform
       const int dlim = lim - (kBlock * e + 32 * h);          // x[t] visible iff t <= dlim
+      // Hidden scores are left in x (their p is zeroed below) and only kept
+      // out of the row max, so the unmasked path carries no select or copy.
+      int mx;
       if (masked) {
+        asm volatile("" ::: "memory");  // keeps the selects inside this branch
+        int y[32];
 #pragma unroll
-        for (int t = 0; t < 32; ++t) x[t] = (t > dlim) ? INT_MIN : x[t];
+        for (int t = 0; t < 32; ++t) y[t] = (t > dlim) ? INT_MIN : x[t];
+        mx = row_max32(y);
+      } else {
+        mx = row_max32(x);
       }
-      int mx = max(max(x[0], x[1]), x[2]);
-#pragma unroll
-      for (int t = 3; t < 31; t += 2) mx = max(max(mx, x[t]), x[t + 1]);
-      mx = max(mx, x[31]);
       mx = half_max(mx);
       const float mt = (kBlock * e <= lim) ? (float)mx * c : -INFINITY;
       const float m_new = fmaxf(m, mt);
@@ -273,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < 32; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)x[t], c, -m_use));
       if (masked) {
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int t = 0; t < 32; ++t) p[t] = (t > dlim) ? 0.0f : p[t];
       }
