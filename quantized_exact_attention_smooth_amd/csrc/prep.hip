@@ -98,24 +98,44 @@ __device__ __forceinline__ float block_max(float x, float* s_red) {
   return x;
 }
 
+// Correctly rounded x / s from r = RN(1 / s): q0 = RN(x r) is within an ulp
+// of x / s and the residual q0 s - x is exact in an fma, so one correction
+// step gives RN(x / s) (Markstein's theorem). The residual is formed as
+// q0 s - x so that x = -0 keeps its sign, as in a division. With
+// s >= 2^-60 the residual cannot underflow unless |x / s| < 2^-24, where
+// int8 and E4M3 codes are 0 whichever way the quotient rounds; below that
+// scale the caller divides.
+constexpr float kFastDivMinScale = 0x1p-60f;
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  const float q0 = x * r;
+  return __builtin_fmaf(-__builtin_fmaf(q0, s, -x), r, q0);
+}
+
 // INT8 codes of one 64-row block of a [L][D] bf16 head (rows >= L are
 // padding: excluded from the absmax and coded 0). sub[c] is subtracted from
-// column c first (the K channel mean; nullptr for Q).
+// column c first (the K channel mean; nullptr for Q). Every load is issued
+// before the block reduction.
 template <int D>
 __device__ void quant_int8_block(const uint16_t* __restrict__ x, int L, int blk,
                                  const float* __restrict__ sub, int8_t* __restrict__ codes,
                                  float* __restrict__ scale, float* s_red) {
   constexpr int kChunks = kBlock * D / 8 / kThreads;  // 8 values per chunk
   constexpr int kLanesPerRow = D / 8;
+  uint4 raw[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const int g = threadIdx.x + kThreads * j;
+    const int row = blk * kBlock + g / kLanesPerRow, c0 = 8 * (g % kLanesPerRow);
+    raw[j] = (row < L) ? *reinterpret_cast<const uint4*>(x + (long)row * D + c0) : make_uint4(0, 0, 0, 0);
+  }
   float f[kChunks][8];
   float a = 0.0f;
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     const int g = threadIdx.x + kThreads * j;
     const int row = blk * kBlock + g / kLanesPerRow, c0 = 8 * (g % kLanesPerRow);
+    unpack8(raw[j], f[j]);
     if (row < L) {
-      uint4 u = *reinterpret_cast<const uint4*>(x + (long)row * D + c0);
-      unpack8(u, f[j]);
       if (sub) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[j][i] = f[j][i] - sub[c0 + i];
@@ -130,52 +150,66 @@ __device__ void quant_int8_block(const uint16_t* __restrict__ x, int L, int blk,
   a = block_max(a, s_red);
   const float s = a / 127.0f;
   if (threadIdx.x == 0) *scale = s;
+  const bool fast = s >= kFastDivMinScale;  // uniform over the block
+  const float r = fast ? 1.0f / s : 0.0f;
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     const int g = threadIdx.x + kThreads * j;
-    const int row = blk * kBlock + g / kLanesPerRow, c0 = 8 * (g % kLanesPerRow);
-    uint32_t lo = 0, hi = 0;
-    if (row < L) {
+    const int c0 = 8 * (g % kLanesPerRow);
+    uint32_t w[2] = {0u, 0u};
+    if (a != 0.0f) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= ((uint32_t)int8_code(f[j][i], s, a) & 0xFFu) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= ((uint32_t)int8_code(f[j][4 + i], s, a) & 0xFFu) << (8 * i);
+      for (int i = 0; i < 8; ++i) {
+        const float q = fast ? div_rn(f[j][i], s, r) : f[j][i] / s;
+        const int code = (int)fminf(fmaxf(rintf(q), -127.0f), 127.0f);
+        w[i >> 2] |= ((uint32_t)code & 0xFFu) << (8 * (i & 3));
+      }
     }
     *reinterpret_cast<uint2*>(codes + (long)(blk * kBlock) * D + (long)(g / kLanesPerRow) * D + c0) =
-        make_uint2(lo, hi);
+        make_uint2(w[0], w[1]);
   }
 }
 
 // E4M3FN codes of one 64-key block of V, written as a [D][64] tile (keys of a
 // channel contiguous). Each work unit codes 4 consecutive keys x 8 channels,
-// so every LDS write is a whole dword of one channel row.
+// so every LDS write is a whole dword of one channel row. The quotient
+// v / sv[c] is rounded to fp32 as an IEEE division would (div_rn, or a
+// division when some scale of the head is tiny) and then converted by the
+// hardware E4M3 conversion (nearest even; |v / sv| <= 448 up to rounding).
 template <int D>
-__device__ void quant_v_block(const uint16_t* __restrict__ v, int L, int blk,
-                              const float* __restrict__ sv, uint8_t* __restrict__ tile,
+__device__ void quant_v_block(const uint16_t* __restrict__ v, int L, int blk, const float* __restrict__ sv,
+                              const float* __restrict__ rv, bool fast, uint8_t* __restrict__ tile,
                               uint8_t* s_tile) {
   constexpr int kUnits = (kBlock / 4) * (D / 8);
-  for (int u = threadIdx.x; u < kUnits; u += kThreads) {
-    const int kq = u % (kBlock / 4), c0 = 8 * (u / (kBlock / 4));
-    uint32_t packed[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed[i] = 0;
+  for (int k = 0; k < (kUnits + kThreads - 1) / kThreads; ++k) {
+    const int u = threadIdx.x + kThreads * k;
+    if (u >= kUnits) break;
+    const int kq = u % (kBlock / 4), c0 = 8 * (u / (kBlock / 4));
+    uint4 raw[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = blk * kBlock + 4 * kq + r;
-      if (row < L) {
-        float f[8];
-        unpack8(*reinterpret_cast<const uint4*>(v + (long)row * D + c0), f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float s = sv[c0 + i];
-          const uint32_t code = (s != 0.0f) ? e4m3_encode_rne(f[i] / s) : 0u;
-          packed[i] |= code << (8 * r);
-        }
-      }
+      raw[r] = (row < L) ? *reinterpret_cast<const uint4*>(v + (long)row * D + c0) : make_uint4(0, 0, 0, 0);
     }
+    float f[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint32_t*>(s_tile + (c0 + i) * kBlock + 4 * kq) = packed[i];
+    for (int r = 0; r < 4; ++r) unpack8(raw[r], f[r]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float s = sv[c0 + i], rc = rv[c0 + i];
+      float q[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool pad = blk * kBlock + 4 * kq + r >= L;
+        q[r] = (pad || s == 0.0f) ? 0.0f : (fast ? div_rn(f[r][i], s, rc) : f[r][i] / s);
+      }
+      int word;
+      asm volatile("" : "=v"(word));  // both halves are written below
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], word, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], word, true);
+      *reinterpret_cast<uint32_t*>(s_tile + (c0 + i) * kBlock + 4 * kq) = (uint32_t)word;
+    }
   }
   __syncthreads();
   constexpr int kOut = D * kBlock / 16 / kThreads;
@@ -186,26 +220,36 @@ __device__ void quant_v_block(const uint16_t* __restrict__ v, int L, int blk,
   }
 }
 
+// One workgroup per (tensor, 64-row block): x in [0, nqb) codes a Q block,
+// [nqb, nqb + nkb) a K block, [nqb + nkb, nqb + 2 nkb) a V block.
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
   __shared__ float s_red[4];
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[D * kBlock];
-  __shared__ float s_mean[D];
-  __shared__ float s_sv[D];
-  const int blk = blockIdx.x;
+  __shared__ float s_ch[D];  // K channel mean, or V channel scale
+  __shared__ float s_rv[D];  // RN(1 / V channel scale)
+  const int job = blockIdx.x;
   const long bh = blockIdx.y;
-  if (threadIdx.x < D) {
-    s_mean[threadIdx.x] = a.k_mean[bh * D + threadIdx.x];
-    s_sv[threadIdx.x] = a.v_scale[bh * D + threadIdx.x];
-  }
-  __syncthreads();
-  if (blk < a.nqb)
-    quant_int8_block<D>(a.q + bh * (long)a.Lq * D, a.Lq, blk, nullptr,
-                        a.q_i8 + bh * (long)a.nqb * kBlock * D, a.q_scale + bh * a.nqb + blk, s_red);
-  if (blk < a.nkb) {
-    quant_int8_block<D>(a.k + bh * (long)a.Lkv * D, a.Lkv, blk, s_mean,
+  if (job < a.nqb) {
+    quant_int8_block<D>(a.q + bh * (long)a.Lq * D, a.Lq, job, nullptr,
+                        a.q_i8 + bh * (long)a.nqb * kBlock * D, a.q_scale + bh * a.nqb + job, s_red);
+  } else if (job < a.nqb + a.nkb) {
+    const int blk = job - a.nqb;
+    if (threadIdx.x < D) s_ch[threadIdx.x] = a.k_mean[bh * D + threadIdx.x];
+    __syncthreads();
+    quant_int8_block<D>(a.k + bh * (long)a.Lkv * D, a.Lkv, blk, s_ch,
                         a.k_i8 + bh * (long)a.nkb * kBlock * D, a.k_scale + bh * a.nkb + blk, s_red);
-    quant_v_block<D>(a.v + bh * (long)a.Lkv * D, a.Lkv, blk, s_sv,
+  } else {
+    const int blk = job - a.nqb - a.nkb;
+    bool tiny = false;
+    if (threadIdx.x < D) {
+      const float s = a.v_scale[bh * D + threadIdx.x];
+      s_ch[threadIdx.x] = s;
+      tiny = s != 0.0f && !(s >= kFastDivMinScale);
+      s_rv[threadIdx.x] = tiny || s == 0.0f ? 0.0f : 1.0f / s;
+    }
+    const bool fast = !__syncthreads_or(tiny);
+    quant_v_block<D>(a.v + bh * (long)a.Lkv * D, a.Lkv, blk, s_ch, s_rv, fast,
                      a.v_fp8 + (bh * a.nkb + blk) * (long)D * kBlock, s_tile);
   }
 }
@@ -215,7 +259,7 @@ int prep_n_split(int Lkv) { return (Lkv + kStatRows - 1) / kStatRows; }
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   const int ns = prep_n_split(a.Lkv);
-  const dim3 g_stats(ns, BH), g_fin(BH), g_quant(a.nqb > a.nkb ? a.nqb : a.nkb, BH);
+  const dim3 g_stats(ns, BH), g_fin(BH), g_quant(a.nqb + 2 * a.nkb, BH);
   if (a.D == 128) {
     prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();

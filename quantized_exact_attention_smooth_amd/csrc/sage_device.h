@@ -24,38 +24,6 @@ __device__ __forceinline__ void unpack8(const uint4& u, float f[8]) {
   f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
 }
 
-// INT8 block code: fp32 quotient (IEEE division) rounded half-to-even,
-// clamped to [-127, 127]; an all-zero block (a == 0) codes to 0.
-__device__ __forceinline__ int int8_code(float x, float s, float a) {
-  if (a == 0.0f) return 0;
-  float r = rintf(x / s);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
-}
-
-// fp32 -> OCP E4M3FN, round to nearest even, saturating to +-448, zero keeps
-// the sign. Normal range: keep 3 of the 23 fraction bits with round-half-even
-// on the 20 dropped bits. Below 2^-6 the code is the nearest multiple of 2^-9
-// (x * 2^9 is exact), which also yields the smallest normal (code 8) when the
-// value rounds up to 2^-6.
-__device__ __forceinline__ uint32_t e4m3_encode_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = fabsf(x);
-  if (!(a < 448.0f)) return (a != a) ? 0x7Fu : (sign | 0x7Eu);
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
-  uint32_t ua = __float_as_uint(a);
-  uint32_t e = ((ua >> 23) & 0xFFu) - 127u + 7u;  // 1..15
-  uint32_t frac = ua & 0x7FFFFFu;
-  uint32_t m = frac >> 20, rem = frac & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) {
-    m += 1u;
-    if (m == 8u) { m = 0u; e += 1u; }
-  }
-  uint32_t code = (e << 3) | m;
-  return sign | (code > 0x7Eu ? 0x7Eu : code);
-}
-
 // Byte offset of 16-byte chunk `chunk` of key row `key` in an LDS K tile of
 // 64 rows x D bytes. The XOR swizzle is linear in the key bits and was chosen
 // so that the A-operand reads of the QK step (16 bytes per lane) and the
