@@ -10,8 +10,15 @@ loop), on inputs already resident in HBM. Prints one JSON line.
             (K back-to-back launches between two HIP events recorded on the
             stream the kernels run on), against the dense INT8/FP8
             matrix-core peak of MI355X (5.0 POPS);
+  scopes    main (sage_attn_fwd_prepped), prep (sage_quant_prep) and
+            end-to-end (sage_attn_fwd, the user-facing call) each timed as
+            back-to-back launches; main also as the p50 and coefficient of
+            variation of 10 batches of 20 launches and as the p50 of 2000
+            single launches, each between its own pair of events;
   cpu_baseline  the CPU oracle (prep + epoch loop) on a bounded sample: one
-            full (b, h) head, rows spread over the host cores.
+            full (b, h) head, rows spread over the host cores, with the
+            full-workload time extrapolated from it; the brute-force fp64
+            reference is timed beside it on the first rows of that head.
 """
 from __future__ import annotations
 
@@ -32,10 +39,14 @@ PEAK_TOPS = 5000.0       # MI355X dense INT8 / FP8 matrix-core peak
 HBM_PEAK_GBS = 8000.0
 
 
+MAIN_KERNEL_SOURCES = ("attn_fwd.hip", "sage_device.h", "sage_launch.h")
+
+
 def _src_hash() -> str:
+    """Hash of the main kernel's sources (the kernel the traffic counters describe)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_exact_attention_smooth_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
+    for n in MAIN_KERNEL_SOURCES:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + f.read())
     return h.hexdigest()[:16]
@@ -67,9 +78,17 @@ def cpu_baseline(w) -> dict:
     oracle.attn_rows_parallel(p, w.causal, w.sm_scale, 0, w.Lq, threads=threads, chunk=64)
     dt = time.perf_counter() - t0
     ops = 4.0 * w.Lq * w.Lkv * w.D / (2 if w.causal else 1)
+    # brute-force fp64 reference on the first rows of the same head
+    n_ref = min(w.Lq, 1024)
+    qf, kf, vf = (oracle.bf16_to_f32(b).astype(np.float64) for b in (qb, kb, vb))
+    t1 = time.perf_counter()
+    oracle.attn_ref_parallel(qf, kf, vf, w.causal, w.sm_scale, 0, n_ref, threads=threads, chunk=64)
+    dt_ref = time.perf_counter() - t1
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"one (b,h) head of {w.name}: preparation + all {w.Lq} query rows, "
-                      f"{dt:.2f} s wall on {threads} threads"}
+                      f"{dt:.2f} s wall on {threads} threads",
+            "full_workload_s_extrapolated": dt * w.B * w.H,
+            "fp64_reference": {"rows": n_ref, "s": dt_ref}}
 
 
 def copy_calibration(nbytes: int, steps: int) -> int:
@@ -158,6 +177,14 @@ def main() -> int:
         prep()
         main_loop()
     torch.cuda.synchronize()
+    # Clock settling: further untimed steps until 0.3 s of GPU work has run,
+    # so that the timed region sees steady-state clocks.
+    settle, t_settle = 0, time.perf_counter()
+    while time.perf_counter() - t_settle < 0.3:
+        prep()
+        main_loop()
+        torch.cuda.synchronize()
+        settle += 1
 
     K = args.steps
     # (1) whole steps, wall clock between two device syncs -> value
@@ -183,6 +210,42 @@ def main() -> int:
 
     main_avg = timed(main_loop)
     prep_avg = timed(prep)
+
+    # end-to-end: sage_attn_fwd into a preallocated workspace
+    nws = ctypes.c_size_t(0)
+    _lib.check("sage_workspace_bytes", L.sage_workspace_bytes(B, H, Lq, Lkv, D, ctypes.byref(nws)))
+    ws = torch.empty(nws.value, dtype=torch.uint8, device=dev)
+    out_e2e = torch.empty_like(out)
+
+    def e2e():
+        _lib.check("sage_attn_fwd", L.sage_attn_fwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out_e2e.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale,
+            ws.data_ptr(), nws.value, sp))
+
+    e2e()
+    e2e_avg = timed(e2e)
+
+    # main kernel: p50 / CV of 10 batches of 20 launches, p50 of single launches
+    batches = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            main_loop()
+        e1.record(stream)
+        e1.synchronize()
+        batches.append(e0.elapsed_time(e1) / 20)
+    n_single = 2000 if main_avg < 1.0 else 50
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_single)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        main_loop()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    singles = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    bsorted = sorted(batches)
+    b_mean = sum(batches) / len(batches)
+    b_cv = math.sqrt(sum((x - b_mean) ** 2 for x in batches) / len(batches)) / b_mean
     ms_step = wall * 1e3 / K
     ops = w.metric_ops
     achieved = ops / (main_avg * 1e-3) / 1e12
@@ -197,8 +260,12 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TOPS, "traffic": _traffic(w.name)},
         "main_ms": main_avg, "main_tops": achieved,
+        "settle_steps": settle,
+        "main_batched_p50_ms": (bsorted[4] + bsorted[5]) / 2, "main_batched_cv": b_cv,
+        "main_single_p50_ms": singles[len(singles) // 2], "main_single_samples": len(singles),
         "prep_ms": prep_avg, "prep_GBps": prep_bytes / (prep_avg * 1e-3) / 1e9,
         "prep_frac_hbm": prep_bytes / (prep_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "e2e_ms": e2e_avg, "e2e_tops": ops / (e2e_avg * 1e-3) / 1e12,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
