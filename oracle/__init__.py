@@ -62,6 +62,8 @@ def _load():
             lib.orc_prep_head.restype = I
             lib.orc_attn_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_float, I, I, P]
             lib.orc_attn_rows.restype = I
+            lib.orc_attn_row_trace.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_float, I, P, P, P, P, P]
+            lib.orc_attn_row_trace.restype = I
             for name in ("orc_attn_unquant_rows", "orc_attn_ref_rows"):
                 getattr(lib, name).argtypes = [P, P, P, I, I, I, I, ctypes.c_double, I, I, P]
                 getattr(lib, name).restype = I
@@ -163,6 +165,27 @@ def attn_rows(prep: dict, causal: bool, sm_scale: float, r0: int = 0, r1: int = 
     if st < 0:
         raise MemoryError("oracle allocation failed")
     return out[r0:r1]
+
+
+def attn_row_trace(prep: dict, causal: bool, sm_scale: float, i: int) -> dict:
+    """Per-epoch checkpoints of query row i of the quantized epoch loop:
+    stats [NKB+1, 4] (m, l, alpha, 0 after each epoch; r, l at the end),
+    p8 [NKB, 64] uint8, pv and ro [NKB, D] float32, out [D] bf16 bits."""
+    Lq, Lkv, D = prep["Lq"], prep["Lkv"], prep["D"]
+    nkb = -(-Lkv // BLOCK)
+    stats = np.zeros((nkb + 1, 4), np.float32)
+    p8 = np.zeros((nkb, BLOCK), np.uint8)
+    pv = np.zeros((nkb, D), np.float32)
+    ro = np.zeros((nkb, D), np.float32)
+    out = np.zeros(D, np.uint16)
+    st = _load().orc_attn_row_trace(_p(prep["q8"]), _p(prep["q_scale"]), _p(prep["k8"]), _p(prep["k_scale"]),
+                                    _p(prep["v8"]), _p(prep["v_scale"]), Lq, Lkv, D, int(bool(causal)),
+                                    float(sm_scale), int(i), _p(out), _p(stats), _p(p8), _p(pv), _p(ro))
+    if st == 2:
+        raise ArithmeticError("INT8 dot product outside the int32-exact range")
+    if st < 0:
+        raise MemoryError("oracle allocation failed")
+    return dict(stats=stats, p8=p8, pv=pv, ro=ro, out=out)
 
 
 def attn_rows_parallel(prep: dict, causal: bool, sm_scale: float, r0: int = 0, r1: int = None,

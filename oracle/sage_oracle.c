@@ -258,10 +258,9 @@ int orc_prep_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int L
 /* ------------------------------------------------ quantized attention (i) */
 
 /*
- * Rows [r0, r1) of one head's output from the prepared operands.
- * Causal masking is bottom-right aligned: row i sees keys j <= i + Lkv - Lq.
- * out: bf16 bits [Lq][D]; only rows r0..r1-1 are written.
- * Returns 0, or 2 if an INT8 dot product left the int32-exact range.
+ * The quantized contract for one query row i of one head, from the
+ * prepared operands. Causal masking is bottom-right aligned: row i sees keys
+ * j <= i + Lkv - Lq.
  *
  * Per row (strict ascending 64-key epochs; Experiment Log, "Phase 1
  * State-Ownership Decision": strict tile order, exact FP8 score bytes,
@@ -278,31 +277,35 @@ int orc_prep_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int L
  * Final conversion: r = 1 / l ("reciprocal"), out = bf16(RO * r * sv[c]);
  * a row with no visible key outputs 0. exp is evaluated in fp64 on the fp32
  * operands and rounded to fp32.
- */
-int orc_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
-                  const uint8_t* v8, const float* v_scale, int Lq, int Lkv, int D, int causal,
-                  float sm_scale, int r0, int r1, uint16_t* out)
+ *
+ * When tr_stats is not NULL the
+ * state after every epoch e (0 <= e < NKB) is copied out, and nothing else
+ * changes: tr_stats[e*4 + 0..3] = m, l, alpha (1 for an epoch without a
+ * visible key, whose state is carried over), 0; tr_stats[NKB*4 + 0..1] =
+ * r, l after the last epoch; tr_p8[e*64 + jj] = P8 of key 64e + jj (0 where
+ * masked); tr_pv[e*D + c] = the epoch's PV partial; tr_ro[e*D + c] = RO
+ * after the epoch. Returns 2 if an accumulator reached 2^24, else 0. */
+static int attn_row(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                    const uint8_t* v8, const float* v_scale, int Lq, int Lkv, int D, int causal,
+                    float sm_scale, int i, float* RO, uint16_t* out_row, float* tr_stats, uint8_t* tr_p8,
+                    float* tr_pv, float* tr_ro)
 {
     int status = 0;
     int nkb = (Lkv + ORC_BLOCK - 1) / ORC_BLOCK;
-    float* RO = (float*)malloc(sizeof(float) * (size_t)D);
-    if (!RO)
-        return -1;
     float z[ORC_BLOCK], p[ORC_BLOCK];
     uint8_t p8[ORC_BLOCK];
+    long last = causal ? (long)i + Lkv - Lq : (long)Lkv - 1; /* last visible key */
+    if (last > Lkv - 1)
+        last = Lkv - 1;
+    float m = -INFINITY, l = 0.0f;
+    for (int c = 0; c < D; ++c)
+        RO[c] = 0.0f;
 
-    for (int i = r0; i < r1; ++i) {
-        long last = causal ? (long)i + Lkv - Lq : (long)Lkv - 1; /* last visible key */
-        if (last > Lkv - 1)
-            last = Lkv - 1;
-        float m = -INFINITY, l = 0.0f;
-        for (int c = 0; c < D; ++c)
-            RO[c] = 0.0f;
-
-        for (int e = 0; e < nkb; ++e) {
-            long j0 = (long)e * ORC_BLOCK;
-            if (j0 > last)
-                break; /* this and every later epoch is fully masked */
+    for (int e = 0; e < nkb; ++e) {
+        long j0 = (long)e * ORC_BLOCK;
+        int live = 0;
+        float alpha = 1.0f;
+        if (j0 <= last) { /* otherwise this and every later epoch is fully masked */
             float sqk = q_scale[i / ORC_BLOCK] * k_scale[e];
             float mx = -INFINITY;
             for (int jj = 0; jj < ORC_BLOCK; ++jj) {
@@ -321,34 +324,93 @@ int orc_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, cons
                     mx = z[jj];
             }
             float mn = m > mx ? m : mx;
-            if (mn == -INFINITY)
-                continue;
-            float alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)m - (double)mn);
-            float ps = 0.0f;
-            for (int jj = 0; jj < ORC_BLOCK; ++jj) {
-                p[jj] = (z[jj] == -INFINITY) ? 0.0f : (float)exp((double)z[jj] - (double)mn);
-                ps += p[jj];
-                p8[jj] = orc_e4m3_encode(p[jj]);
-            }
-            l = l * alpha + ps;
-            for (int c = 0; c < D; ++c) {
-                float pv = 0.0f;
+            if (mn != -INFINITY) {
+                live = 1;
+                alpha = (m == -INFINITY) ? 0.0f : (float)exp((double)m - (double)mn);
+                float ps = 0.0f;
                 for (int jj = 0; jj < ORC_BLOCK; ++jj) {
-                    long j = j0 + jj;
-                    if (j >= Lkv)
-                        break; /* padded keys have P8 = 0 and V8 = 0 */
-                    pv += (float)orc_e4m3_decode(p8[jj]) * (float)orc_e4m3_decode(v8[j * D + c]);
+                    p[jj] = (z[jj] == -INFINITY) ? 0.0f : (float)exp((double)z[jj] - (double)mn);
+                    ps += p[jj];
+                    p8[jj] = orc_e4m3_encode(p[jj]);
                 }
-                RO[c] = RO[c] * alpha + pv;
+                l = l * alpha + ps;
+                for (int c = 0; c < D; ++c) {
+                    float pv = 0.0f;
+                    for (int jj = 0; jj < ORC_BLOCK; ++jj) {
+                        long j = j0 + jj;
+                        if (j >= Lkv)
+                            break; /* padded keys have P8 = 0 and V8 = 0 */
+                        pv += (float)orc_e4m3_decode(p8[jj]) * (float)orc_e4m3_decode(v8[j * D + c]);
+                    }
+                    RO[c] = RO[c] * alpha + pv;
+                    if (tr_pv)
+                        tr_pv[(long)e * D + c] = pv;
+                }
+                m = mn;
             }
-            m = mn;
         }
-        float r = (l > 0.0f) ? 1.0f / l : 0.0f;
-        for (int c = 0; c < D; ++c)
-            out[(long)i * D + c] = orc_f32_to_bf16((RO[c] * r) * v_scale[c]);
+        if (tr_stats) {
+            tr_stats[e * 4 + 0] = m;
+            tr_stats[e * 4 + 1] = l;
+            tr_stats[e * 4 + 2] = alpha;
+            tr_stats[e * 4 + 3] = 0.0f;
+            for (int jj = 0; jj < ORC_BLOCK; ++jj)
+                tr_p8[(long)e * ORC_BLOCK + jj] = live ? p8[jj] : 0;
+            for (int c = 0; c < D; ++c) {
+                if (!live)
+                    tr_pv[(long)e * D + c] = 0.0f;
+                tr_ro[(long)e * D + c] = RO[c];
+            }
+        }
+    }
+    float r = (l > 0.0f) ? 1.0f / l : 0.0f;
+    if (tr_stats) {
+        tr_stats[nkb * 4 + 0] = r;
+        tr_stats[nkb * 4 + 1] = l;
+        tr_stats[nkb * 4 + 2] = 0.0f;
+        tr_stats[nkb * 4 + 3] = 0.0f;
+    }
+    for (int c = 0; c < D; ++c)
+        out_row[c] = orc_f32_to_bf16((RO[c] * r) * v_scale[c]);
+    return status;
+}
+
+/* Rows [r0, r1) of one head's output. out: bf16 bits [Lq][D]; only rows
+ * r0..r1-1 are written. Returns 0, or 2 if an INT8 dot product left the
+ * int32-exact range. */
+int orc_attn_rows(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                  const uint8_t* v8, const float* v_scale, int Lq, int Lkv, int D, int causal,
+                  float sm_scale, int r0, int r1, uint16_t* out)
+{
+    int status = 0;
+    float* RO = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!RO)
+        return -1;
+    for (int i = r0; i < r1; ++i) {
+        int st = attn_row(q8, q_scale, k8, k_scale, v8, v_scale, Lq, Lkv, D, causal, sm_scale, i, RO,
+                          out + (long)i * D, NULL, NULL, NULL, NULL);
+        if (st)
+            status = st;
     }
     free(RO);
     return status;
+}
+
+/* Per-epoch checkpoints of one row i (the Phase 2B checkpoint list: m, d,
+ * FP8 probability, rescale, PV, FP32 RO, reciprocal), laid out as in
+ * attn_row. out_row receives the row's bf16 output. */
+int orc_attn_row_trace(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale,
+                       const uint8_t* v8, const float* v_scale, int Lq, int Lkv, int D, int causal,
+                       float sm_scale, int i, uint16_t* out_row, float* tr_stats, uint8_t* tr_p8, float* tr_pv,
+                       float* tr_ro)
+{
+    float* RO = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!RO)
+        return -1;
+    int st = attn_row(q8, q_scale, k8, k_scale, v8, v_scale, Lq, Lkv, D, causal, sm_scale, i, RO, out_row,
+                      tr_stats, tr_p8, tr_pv, tr_ro);
+    free(RO);
+    return st;
 }
 
 /* ------------------------------------- unquantized epoch loop, fp64 (ii) */
