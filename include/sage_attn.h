@@ -122,6 +122,28 @@ int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, in
                         const int* tiles, int n_tiles, int32_t* acc_out, void* stream);
 
 /*
+ * Debug: per-epoch checkpoints of 32 query rows (Experiment Log, "Phase 2B
+ * Fixed Aligned Numerical Prototype": the QK, m, d, FP8 probability,
+ * rescale, PV, FP32 RO and reciprocal checkpoints). Runs the main loop's own
+ * kernel on the one 128-row tile of head (b, h) that holds rows row0 ..
+ * row0 + 31 (row0 a multiple of 32, < Lq); the wave owning those rows
+ * writes, for row t = row0 + i and every epoch e it computes (e below the
+ * wave's epoch count; the caller pre-fills the buffers to recognise the rest):
+ *   stats [32][NKB+1][4] fp32: [i][e] = m (log2 domain: max of z * log2(e)),
+ *         l, alpha (of this epoch), 0; [i][NKB] = 1/l, l at the end;
+ *   p8    [32][NKB][64] uint8: the epoch's E4M3 P bytes, key 64e + j;
+ *   ro    [32][NKB][D]  fp32: RO after the epoch (RO * alpha + PV).
+ * PV itself is not a separate value on this hardware: the matrix core adds
+ * it into RO. out (bf16 [B][H][Lq][D]) receives that tile's rows as the
+ * main loop would write them. Arguments otherwise as sage_attn_fwd_prepped;
+ * stats 16-byte aligned, p8 and ro 4-byte aligned.
+ */
+int sage_debug_epoch_trace(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                           const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
+                           int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, int b, int h,
+                           int row0, float* stats, uint8_t* p8, float* ro, void* stream);
+
+/*
  * Debug: run the device conversions the main loop uses on n fp32 values x
  * (device): p8[i] = FP8 E4M3FN code as the probability packing produces it,
  * bf16[i] = bf16 bits as the output conversion produces them.

@@ -15,7 +15,7 @@ import torch
 from ._lib import (LIB_PATH, SAGE_BLOCK, SageError, check, lib, status_str)  # noqa: F401
 
 __all__ = ["workspace_bytes", "prep_scratch_bytes", "quant_prep", "attn_fwd_prepped", "attn_fwd",
-           "debug_qk_int32", "debug_codecs", "SageError", "status_str", "LIB_PATH"]
+           "debug_qk_int32", "debug_codecs", "debug_epoch_trace", "SageError", "status_str", "LIB_PATH"]
 
 
 def _stream(stream=None) -> int:
@@ -113,6 +113,29 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, sm
                              _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     check("sage_attn_fwd", st)
     return out
+
+
+def debug_epoch_trace(prep: dict, b: int, h: int, row0: int, causal: bool, sm_scale: float = None,
+                      stream=None) -> dict:
+    """sage_debug_epoch_trace: per-epoch checkpoints of rows row0 .. row0+31 of
+    head (b, h). Returns stats [32, NKB+1, 4] (NaN where not written), p8
+    [32, NKB, 64] uint8 (0xFF where not written), ro [32, NKB, D] and out."""
+    B, H, Lq, Lkv, D = prep["shape"]
+    nkb = -(-Lkv // SAGE_BLOCK)
+    dev = prep["q_i8"].device
+    stats = torch.full((32, nkb + 1, 4), float("nan"), dtype=torch.float32, device=dev)
+    p8 = torch.full((32, nkb, SAGE_BLOCK), 0xFF, dtype=torch.uint8, device=dev)
+    ro = torch.full((32, nkb, D), float("nan"), dtype=torch.float32, device=dev)
+    out = torch.zeros((B, H, Lq, D), dtype=torch.bfloat16, device=dev)
+    st = lib().sage_debug_epoch_trace(
+        _dev(prep["q_i8"], torch.int8, "q_i8"), _dev(prep["q_scale"], torch.float32, "q_scale"),
+        _dev(prep["k_i8"], torch.int8, "k_i8"), _dev(prep["k_scale"], torch.float32, "k_scale"),
+        _dev(prep["v_fp8"], torch.uint8, "v_fp8"), _dev(prep["v_scale"], torch.float32, "v_scale"),
+        _dev(out, torch.bfloat16, "out"), B, H, Lq, Lkv, D, int(bool(causal)),
+        float(sm_scale) if sm_scale else 0.0, int(b), int(h), int(row0), stats.data_ptr(), p8.data_ptr(),
+        ro.data_ptr(), _stream(stream))
+    check("sage_debug_epoch_trace", st)
+    return dict(stats=stats, p8=p8, ro=ro, out=out)
 
 
 def debug_qk_int32(prep: dict, tiles, stream=None) -> torch.Tensor:

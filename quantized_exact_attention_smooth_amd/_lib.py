@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
             L.sage_debug_qk_int32.restype = I
             L.sage_debug_codecs.argtypes = [P, I, P, P, P]
             L.sage_debug_codecs.restype = I
+            L.sage_debug_epoch_trace.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P, P, P, P]
+            L.sage_debug_epoch_trace.restype = I
             _lib = L
     return _lib
 

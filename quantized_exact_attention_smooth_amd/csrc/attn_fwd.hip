@@ -175,7 +175,7 @@ __device__ __forceinline__ float half_sum(float x) {
 // The QK results of step 2 and the PV results of step 4 are consumed one body
 // later, so neither matrix-core latency is exposed to the softmax.
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool TRACE>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   // Four separate LDS objects (not one array) so that the compiler can tell
   // the in-flight direct fills apart from the buffers being read.
@@ -185,8 +185,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_v1[D * kBlock];
 
   const int BH = a.B * a.H;
-  const int tile = a.n_qtiles - 1 - (int)(blockIdx.x / BH);
-  const long bh = blockIdx.x % BH;
+  const int tile = TRACE ? a.trace_tile : a.n_qtiles - 1 - (int)(blockIdx.x / BH);
+  const long bh = TRACE ? (long)a.trace_bh : (long)(blockIdx.x % BH);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int h = lane >> 5, ql = lane & 31;
@@ -319,6 +319,25 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
         ro[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, ro[cb], 0, 0, 0, 127, 0, 127);
       }
       m = m_new;
+      if (TRACE && w == a.trace_wave) {
+        // Checkpoints of this epoch: m (log2 domain), l, alpha, P8, RO.
+        const float lt = half_sum(l);
+        if (h == 0) {
+          float* st = a.tr_stats + ((long)ql * (a.nkb + 1) + e) * 4;
+          st[0] = m;
+          st[1] = lt;
+          st[2] = alpha;
+          st[3] = 0.0f;
+        }
+        uint32_t* p8 = reinterpret_cast<uint32_t*>(a.tr_p8 + ((long)ql * a.nkb + e) * kBlock + 32 * h);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) p8[d] = (uint32_t)pb[d];
+        float* rt = a.tr_ro + ((long)ql * a.nkb + e) * D;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) rt[32 * cb + 8 * (r / 4) + 4 * h + r % 4] = ro[cb][r];
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -332,6 +351,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   // Epilogue: the two halves of a query hold partial sums of l.
   const float lt = half_sum(l);
   const float rcp = (lt > 0.0f) ? 1.0f / lt : 0.0f;
+  if (TRACE && w == a.trace_wave && h == 0) {
+    float* st = a.tr_stats + ((long)ql * (a.nkb + 1) + a.nkb) * 4;
+    st[0] = rcp;
+    st[1] = lt;
+    st[2] = 0.0f;
+    st[3] = 0.0f;
+  }
   if (qrow < a.Lq) {
     uint16_t* orow = a.out + (bh * a.Lq + qrow) * (long)D;
     const float* svh = a.v_scale + bh * D;
@@ -401,16 +427,23 @@ __global__ __launch_bounds__(256) void codecs_debug_kernel(const float* __restri
 
 // ------------------------------------------------------------ launchers
 
-template <int D, bool C>
+template <int D, bool C, bool T>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
-  const long blocks = (long)a.n_qtiles * a.B * a.H;
-  attn_fwd_kernel<D, C><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
+  const long blocks = T ? 1L : (long)a.n_qtiles * a.B * a.H;
+  attn_fwd_kernel<D, C, T><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  if (D == 128) return causal ? launch_attn_t<128, true>(a, stream) : launch_attn_t<128, false>(a, stream);
-  return causal ? launch_attn_t<64, true>(a, stream) : launch_attn_t<64, false>(a, stream);
+  if (D == 128)
+    return causal ? launch_attn_t<128, true, false>(a, stream) : launch_attn_t<128, false, false>(a, stream);
+  return causal ? launch_attn_t<64, true, false>(a, stream) : launch_attn_t<64, false, false>(a, stream);
+}
+
+hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
+  if (D == 128)
+    return causal ? launch_attn_t<128, true, true>(a, stream) : launch_attn_t<128, false, true>(a, stream);
+  return causal ? launch_attn_t<64, true, true>(a, stream) : launch_attn_t<64, false, true>(a, stream);
 }
 
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream) {

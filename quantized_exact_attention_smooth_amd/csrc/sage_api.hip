@@ -112,9 +112,14 @@ int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, i
   return hip_status(sage::launch_prep(a, (hipStream_t)stream));
 }
 
-int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
-                          const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
-                          int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument block shared by the main-loop entry points.
+int attn_args(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+              const uint8_t* v_fp8, const float* v_scale, void* out, int B, int H, int Lq, int Lkv, int D,
+              int causal, float sm_scale, sage::AttnArgs* a) {
   const int st = check_dims(B, H, Lq, Lkv, D);
   if (st != SAGE_OK) return st;
   if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_fp8 || !v_scale || !out) return SAGE_ERR_INVALID_ARG;
@@ -124,15 +129,49 @@ int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t
   if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
   if (isnan(sm_scale) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
   if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
+  *a = sage::AttnArgs{};
+  a->q_i8 = q_i8; a->q_scale = q_scale; a->k_i8 = k_i8; a->k_scale = k_scale;
+  a->v_fp8 = v_fp8; a->v_scale = v_scale; a->out = (uint16_t*)out;
+  a->B = B; a->H = H; a->Lq = Lq; a->Lkv = Lkv;
+  a->nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
+  a->nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
+  a->n_qtiles = (Lq + sage::kQTile - 1) / sage::kQTile;
+  a->scale_log2 = sm_scale * 1.4426950408889634f;
+  return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                          const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
+                          int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, void* stream) {
   sage::AttnArgs a;
-  a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale;
-  a.v_fp8 = v_fp8; a.v_scale = v_scale; a.out = (uint16_t*)out;
-  a.B = B; a.H = H; a.Lq = Lq; a.Lkv = Lkv;
-  a.nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
-  a.nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
-  a.n_qtiles = (Lq + sage::kQTile - 1) / sage::kQTile;
-  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  const int st = attn_args(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, out, B, H, Lq, Lkv, D, causal,
+                           sm_scale, &a);
+  if (st != SAGE_OK) return st;
   return hip_status(sage::launch_attn(a, D, causal == 1, (hipStream_t)stream));
+}
+
+int sage_debug_epoch_trace(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                           const uint8_t* v_fp8, const float* v_scale, void* out, int B, int H, int Lq, int Lkv,
+                           int D, int causal, float sm_scale, int b, int h, int row0, float* stats,
+                           uint8_t* p8, float* ro, void* stream) {
+  sage::AttnArgs a;
+  const int st = attn_args(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, out, B, H, Lq, Lkv, D, causal,
+                           sm_scale, &a);
+  if (st != SAGE_OK) return st;
+  if (b < 0 || b >= B || h < 0 || h >= H || row0 < 0 || row0 >= Lq || row0 % 32 != 0) return SAGE_ERR_INVALID_ARG;
+  if (!stats || !p8 || !ro || misaligned(stats, 16) || misaligned(p8, 4) || misaligned(ro, 4))
+    return SAGE_ERR_INVALID_ARG;
+  a.trace_bh = b * H + h;
+  a.trace_tile = row0 / sage::kQTile;
+  a.trace_wave = (row0 % sage::kQTile) / 32;
+  a.tr_stats = stats;
+  a.tr_p8 = p8;
+  a.tr_ro = ro;
+  return hip_status(sage::launch_attn_trace(a, D, causal == 1, (hipStream_t)stream));
 }
 
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,

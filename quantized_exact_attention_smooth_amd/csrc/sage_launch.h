@@ -37,6 +37,13 @@ struct AttnArgs {
   uint16_t* out;
   int B, H, Lq, Lkv, nqb, nkb, n_qtiles;
   float scale_log2;  // sm_scale * log2(e)
+  // Per-epoch checkpoints (trace launches only): the workgroup runs tile
+  // trace_tile of head trace_bh, and wave trace_wave writes its 32 rows'
+  // state after every epoch (layouts in sage_attn.h).
+  int trace_bh, trace_tile, trace_wave;
+  float* tr_stats;
+  uint8_t* tr_p8;
+  float* tr_ro;
 };
 
 constexpr int kMaxDebugTiles = 64;
@@ -51,6 +58,7 @@ struct QkDebugArgs {
 int prep_n_split(int Lkv);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream);
+hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream);
 hipError_t launch_codecs_debug(const float* x, int n, uint8_t* p8, uint16_t* bf16, hipStream_t stream);
 

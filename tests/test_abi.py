@@ -31,7 +31,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("sage_quant_prep", "sage_attn_fwd", "sage_attn_fwd_prepped", "sage_workspace_bytes",
-              "sage_prep_scratch_bytes", "sage_debug_qk_int32", "sage_debug_codecs", "sage_status_str"):
+              "sage_prep_scratch_bytes", "sage_debug_qk_int32", "sage_debug_codecs", "sage_debug_epoch_trace",
+              "sage_status_str"):
         assert n in names
 
 
@@ -116,4 +117,11 @@ def test_debug_qk_rejects_out_of_range_tiles(lib):
     neg = (ctypes.c_int * 4)(0, -1, 0, 0)
     assert lib.sage_debug_qk_int32(FAKE, FAKE, 1, 1, 128, 128, 64, neg, 1, FAKE, None) == -1
     assert lib.sage_debug_codecs(None, 4, FAKE, FAKE, None) == -1
+    t = lib.sage_debug_epoch_trace
+    ok = [FAKE] * 7 + [2, 3, 128, 128, 64, 1, 0.0]
+    assert t(*ok, 2, 0, 0, FAKE, FAKE, FAKE, None) == -1       # b out of range
+    assert t(*ok, 0, 3, 0, FAKE, FAKE, FAKE, None) == -1       # h out of range
+    assert t(*ok, 0, 0, 16, FAKE, FAKE, FAKE, None) == -1      # row0 not a multiple of 32
+    assert t(*ok, 0, 0, 128, FAKE, FAKE, FAKE, None) == -1     # row0 >= Lq
+    assert t(*ok, 0, 0, 0, None, FAKE, FAKE, None) == -1       # missing output
     assert lib.sage_debug_codecs(FAKE, 0, FAKE, FAKE, None) == 0

@@ -1,0 +1,90 @@
+"""Per-epoch checkpoints of the main loop against the oracle's own (Experiment
+Log, "Phase 2B Fixed Aligned Numerical Prototype": the m, d, FP8 probability,
+rescale, FP32 RO and reciprocal checkpoints, here after every epoch).
+
+sage_debug_epoch_trace runs the main kernel itself on one tile and records the
+state of 32 rows after each epoch it computes. Against oracle.attn_row_trace
+on the same bf16 inputs:
+  m      the kernel keeps z * log2(e) (it uses exp2): |m_gpu - m * log2 e|
+         <= 1e-5 * max(1, |m|); -inf exactly where the oracle has -inf;
+  l      relative 2e-5; alpha absolute 2e-5; 1/l relative 2e-5;
+  P8     the same E4M3 byte, except where exp and exp2 round a p across a
+         code boundary: such bytes differ by one code and are at most 1e-3
+         of the bytes compared;
+  RO     fp32 sums of exact fp8 products in another order: max-abs within
+         1e-3 of the epoch's largest |RO|;
+and the output rows the trace launch writes equal the main kernel's bit for
+bit. Epochs past the wave's last one are not computed; the oracle's state
+must be unchanged there.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+import quantized_exact_attention_smooth_amd as sage
+from _parity import oracle_preps, say
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+CASES = {
+    0: [(0, 0, 0), (0, 0, 32), (0, 0, 64), (0, 0, 96)],            # every wave of Q128 x KV192
+    1: [(0, 0, 0), (0, 7, 512), (0, 3, 992)],                        # ragged causal L=1000: first, middle, last
+    2: [(1, 5, 0), (0, 20, 2016), (1, 31, 4064)],                    # headline: top, middle, bottom of a head
+    4: [(2, 9, 4096)],                                               # D=64 Student-t with outlier channels
+}
+
+
+@pytest.mark.parametrize("wi", sorted(CASES))
+def test_epoch_checkpoints_match_the_oracle(wi, gpu_device):
+    w = si.WORKLOADS[wi]
+    say(f"epoch trace: {w.name} rows {CASES[wi]}")
+    q, k, v = si.workload_qkv(w)
+    pr = sage.quant_prep(q.to(gpu_device), k.to(gpu_device), v.to(gpu_device))
+    full = sage.attn_fwd_prepped(pr, w.causal, w.sm_scale)
+    torch.cuda.synchronize()
+    full_bits = si.bf16_bits(full)
+    preps = oracle_preps(q, k, v, sorted({(b, h) for b, h, _ in CASES[wi]}))
+    nkb = -(-w.Lkv // 64)
+    p8_total = p8_diff = 0
+    for b, h, row0 in CASES[wi]:
+        t = sage.debug_epoch_trace(pr, b, h, row0, w.causal, w.sm_scale)
+        torch.cuda.synchronize()
+        st, p8, ro = t["stats"].cpu().numpy(), t["p8"].cpu().numpy(), t["ro"].cpu().numpy()
+        out_bits = si.bf16_bits(t["out"])
+        rows = range(row0, min(row0 + 32, w.Lq))
+        assert np.array_equal(out_bits[b, h, row0:rows.stop], full_bits[b, h, row0:rows.stop]), (b, h, row0)
+        n_done = int(np.sum(~np.isnan(st[0, :nkb, 1])))  # epochs the wave computed (same for its 32 rows)
+        assert n_done >= 1
+        for i, row in enumerate(rows):
+            o = oracle.attn_row_trace(preps[(b, h)], w.causal, w.sm_scale, row)
+            what = f"{w.name} head ({b},{h}) row {row}"
+            assert np.all(~np.isnan(st[i, :n_done, 1])) and np.all(np.isnan(st[i, n_done:nkb, 1])), what
+            for e in range(n_done):
+                mo, lo_, ao = (float(x) for x in o["stats"][e, :3])
+                mg, lg, ag = (float(x) for x in st[i, e, :3])
+                if mo == -np.inf:
+                    assert mg == -np.inf and lg == 0.0, (what, e)
+                    continue
+                assert abs(mg - mo * LOG2E) <= 1e-5 * max(1.0, abs(mo * LOG2E)), (what, e, mg, mo * LOG2E)
+                assert abs(lg - lo_) <= 2e-5 * lo_, (what, e, lg, lo_)
+                assert abs(ag - ao) <= 2e-5, (what, e, ag, ao)
+                d = np.abs(p8[i, e].astype(np.int32) - o["p8"][e].astype(np.int32))
+                assert d.max() <= 1, (what, e, np.flatnonzero(d > 1)[:5])
+                p8_total += d.size
+                p8_diff += int(np.count_nonzero(d))
+                scale = float(np.abs(o["ro"][e]).max())
+                err = float(np.abs(ro[i, e].astype(np.float64) - o["ro"][e]).max())
+                assert err <= 1e-3 * scale + 1e-30, (what, e, err, scale)
+            # epochs the wave did not compute change nothing in the oracle either
+            for e in range(n_done, nkb):
+                assert np.array_equal(o["stats"][e, :2], o["stats"][n_done - 1, :2]) and not o["p8"][e].any(), \
+                    (what, e)
+            rg, lg_end = float(st[i, nkb, 0]), float(st[i, nkb, 1])
+            ro_, lo_end = float(o["stats"][nkb, 0]), float(o["stats"][nkb, 1])
+            assert abs(lg_end - lo_end) <= 2e-5 * lo_end and abs(rg - ro_) <= 2e-5 * ro_, (what, rg, ro_)
+    say(f"  P8 bytes compared {p8_total}, differing by one code {p8_diff}")
+    assert p8_diff <= 1e-3 * p8_total
