@@ -162,6 +162,10 @@ __device__ __forceinline__ float half_sum(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
+// s_waitcnt with lgkmcnt(0) and the vector-memory and export counters left
+// at their maxima: LDS operations done, global loads and fills still in flight.
+constexpr int kWaitLgkmOnly = 0xC07F;
+
 // ------------------------------------------------------------ main kernel
 //
 // Software pipeline per wave, one body per epoch e:
@@ -175,7 +179,7 @@ __device__ __forceinline__ float half_sum(float x) {
 // The QK results of step 2 and the PV results of step 4 are consumed one body
 // later, so neither matrix-core latency is exposed to the softmax.
 
-template <int D, bool CAUSAL, bool TRACE>
+template <int D, bool CAUSAL, bool TRACE, bool QBF16>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   // Four separate LDS objects (not one array) so that the compiler can tell
   // the in-flight direct fills apart from the buffers being read.
@@ -212,15 +216,77 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   const int lim = CAUSAL ? min(qrow + off, a.Lkv - 1) : a.Lkv - 1;
   const int w_lim = CAUSAL ? min(wrow0 + off, a.Lkv - 1) : a.Lkv - 1;
 
+  // The first K/V fills start before the Q codes are set up, so that their
+  // latency overlaps the Q loads.
+  const int8_t* kh = a.k_i8 + bh * (long)a.nkb * kBlock * D;
+  const uint8_t* vh = a.v_fp8 + bh * (long)a.nkb * D * kBlock;
+  // k_scale is read-only for the kernel's lifetime: scalar (constant-space) loads.
+  const __attribute__((address_space(4))) float* ksh =
+      (const __attribute__((address_space(4))) float*)(a.k_scale + bh * a.nkb);
+  if (n_ep > 0) {
+    k_tile_to_lds<D>(kh, s_k0, w, lane);
+    v_tile_to_lds<D>(vh, s_v0, w, lane);
+    if (n_ep > 1) k_tile_to_lds<D>(kh + kBlock * D, s_k1, w, lane);
+  }
+
   v4i qreg[D / 32];
-  {
+  float sq;
+  if constexpr (QBF16) {
+    // Q quantized here from bf16, as the preparation pass would: this lane
+    // codes row qrow, columns 32s + 16h .. +15; the 64-row block's scale is
+    // the absmax over the two waves that own the block (rows >= Lq count 0
+    // and code 0).
+    __shared__ float s_qmax[kThreads / 64];
+    float f[D / 32][16];
+    float am = 0.0f;
+    const uint16_t* qsrc = a.q_bf16 + (bh * a.Lq + qrow) * (long)D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      uint4 u0 = make_uint4(0u, 0u, 0u, 0u), u1 = u0;
+      if (qrow < a.Lq) {
+        u0 = *reinterpret_cast<const uint4*>(qsrc + 32 * s + 16 * h);
+        u1 = *reinterpret_cast<const uint4*>(qsrc + 32 * s + 16 * h + 8);
+      }
+      unpack8(u0, f[s]);
+      unpack8(u1, f[s] + 8);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(f[s][j]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    if (lane == 0) s_qmax[w] = am;
+    // LDS exchange only: wait for this wave's LDS write, not for the K/V
+    // fills in flight.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkmOnly);
+    asm volatile("s_barrier" ::: "memory");
+    const float qa = fmaxf(s_qmax[w & ~1], s_qmax[w | 1]);
+    const float s_q = qa / 127.0f;
+    const bool fast = s_q >= kFastDivMinScale;
+    const float rq = fast ? 1.0f / s_q : 0.0f;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t word = 0u;
+        if (qa != 0.0f) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = f[s][4 * d + j];
+            word |= code_i8(fast ? div_rn(x, s_q, rq) : x / s_q) << (8 * j);
+          }
+        }
+        qreg[s][d] = (int)word;
+      }
+    }
+    sq = wave_on ? s_q : 0.0f;
+  } else {
     const int8_t* qh = a.q_i8 + bh * (long)a.nqb * kBlock * D;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
       qreg[s] = (qrow < a.Lq) ? *reinterpret_cast<const v4i*>(qh + (long)qrow * D + 32 * s + 16 * h)
                               : v4i{};
+    sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
   }
-  const float sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
   const float cq = sq * a.scale_log2;
 
   float m = -INFINITY, l = 0.0f;
@@ -228,19 +294,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) ro[cb] = v16f{};
 
-  const int8_t* kh = a.k_i8 + bh * (long)a.nkb * kBlock * D;
-  const uint8_t* vh = a.v_fp8 + bh * (long)a.nkb * D * kBlock;
-  // k_scale is read-only for the kernel's lifetime: scalar (constant-space) loads.
-  const __attribute__((address_space(4))) float* ksh =
-      (const __attribute__((address_space(4))) float*)(a.k_scale + bh * a.nkb);
-
   v16i sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
-  if (n_ep > 0) {
-    k_tile_to_lds<D>(kh, s_k0, w, lane);
-    v_tile_to_lds<D>(vh, s_v0, w, lane);
-    if (n_ep > 1) k_tile_to_lds<D>(kh + kBlock * D, s_k1, w, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-  }
+  __builtin_amdgcn_s_waitcnt(0);  // the first K/V fills (issued above) have landed
   __syncthreads();
   if (w_ep > 0) qk_epoch<D>(s_k0, qreg, lane, sa0, sa1);
   // The first epoch refills s_k0 with K(2): every wave must have read K(0) first.
@@ -427,23 +482,28 @@ __global__ __launch_bounds__(256) void codecs_debug_kernel(const float* __restri
 
 // ------------------------------------------------------------ launchers
 
-template <int D, bool C, bool T>
+template <int D, bool C, bool T, bool QB>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   const long blocks = T ? 1L : (long)a.n_qtiles * a.B * a.H;
-  attn_fwd_kernel<D, C, T><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
+  attn_fwd_kernel<D, C, T, QB><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
+template <bool T, bool QB>
+static hipError_t launch_attn_v(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
   if (D == 128)
-    return causal ? launch_attn_t<128, true, false>(a, stream) : launch_attn_t<128, false, false>(a, stream);
-  return causal ? launch_attn_t<64, true, false>(a, stream) : launch_attn_t<64, false, false>(a, stream);
+    return causal ? launch_attn_t<128, true, T, QB>(a, stream) : launch_attn_t<128, false, T, QB>(a, stream);
+  return causal ? launch_attn_t<64, true, T, QB>(a, stream) : launch_attn_t<64, false, T, QB>(a, stream);
 }
 
+hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
+  return launch_attn_v<false, false>(a, D, causal, stream);
+}
 hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  if (D == 128)
-    return causal ? launch_attn_t<128, true, true>(a, stream) : launch_attn_t<128, false, true>(a, stream);
-  return causal ? launch_attn_t<64, true, true>(a, stream) : launch_attn_t<64, false, true>(a, stream);
+  return launch_attn_v<true, false>(a, D, causal, stream);
+}
+hipError_t launch_attn_fused_q(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
+  return launch_attn_v<false, true>(a, D, causal, stream);
 }
 
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream) {

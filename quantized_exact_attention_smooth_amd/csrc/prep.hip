@@ -98,19 +98,6 @@ __device__ __forceinline__ float block_max(float x, float* s_red) {
   return x;
 }
 
-// Correctly rounded x / s from r = RN(1 / s): q0 = RN(x r) is within an ulp
-// of x / s and the residual q0 s - x is exact in an fma, so one correction
-// step gives RN(x / s) (Markstein's theorem). The residual is formed as
-// q0 s - x so that x = -0 keeps its sign, as in a division. With
-// s >= 2^-60 the residual cannot underflow unless |x / s| < 2^-24, where
-// int8 and E4M3 codes are 0 whichever way the quotient rounds; below that
-// scale the caller divides.
-constexpr float kFastDivMinScale = 0x1p-60f;
-__device__ __forceinline__ float div_rn(float x, float s, float r) {
-  const float q0 = x * r;
-  return __builtin_fmaf(-__builtin_fmaf(q0, s, -x), r, q0);
-}
-
 // INT8 codes of one 64-row block of a [L][D] bf16 head (rows >= L are
 // padding: excluded from the absmax and coded 0). sub[c] is subtracted from
 // column c first (the K channel mean; nullptr for Q). Every load is issued
@@ -161,8 +148,7 @@ __device__ void quant_int8_block(const uint16_t* __restrict__ x, int L, int blk,
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float q = fast ? div_rn(f[j][i], s, r) : f[j][i] / s;
-        const int code = (int)fminf(fmaxf(rintf(q), -127.0f), 127.0f);
-        w[i >> 2] |= ((uint32_t)code & 0xFFu) << (8 * (i & 3));
+        w[i >> 2] |= code_i8(q) << (8 * (i & 3));
       }
     }
     *reinterpret_cast<uint2*>(codes + (long)(blk * kBlock) * D + (long)(g / kLanesPerRow) * D + c0) =
@@ -220,15 +206,16 @@ __device__ void quant_v_block(const uint16_t* __restrict__ v, int L, int blk, co
   }
 }
 
-// One workgroup per (tensor, 64-row block): x in [0, nqb) codes a Q block,
-// [nqb, nqb + nkb) a K block, [nqb + nkb, nqb + 2 nkb) a V block.
+// One workgroup per (tensor, 64-row block): job in [0, nqb) codes a Q block,
+// [nqb, nqb + nkb) a K block, [nqb + nkb, nqb + 2 nkb) a V block. With
+// a.skip_q the grid covers the K and V jobs only.
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
   __shared__ float s_red[4];
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[D * kBlock];
   __shared__ float s_ch[D];  // K channel mean, or V channel scale
   __shared__ float s_rv[D];  // RN(1 / V channel scale)
-  const int job = blockIdx.x;
+  const int job = blockIdx.x + (a.skip_q ? a.nqb : 0);
   const long bh = blockIdx.y;
   if (job < a.nqb) {
     quant_int8_block<D>(a.q + bh * (long)a.Lq * D, a.Lq, job, nullptr,
@@ -259,7 +246,7 @@ int prep_n_split(int Lkv) { return (Lkv + kStatRows - 1) / kStatRows; }
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   const int ns = prep_n_split(a.Lkv);
-  const dim3 g_stats(ns, BH), g_fin(BH), g_quant(a.nqb + 2 * a.nkb, BH);
+  const dim3 g_stats(ns, BH), g_fin(BH), g_quant((a.skip_q ? 0 : a.nqb) + 2 * a.nkb, BH);
   if (a.D == 128) {
     prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();

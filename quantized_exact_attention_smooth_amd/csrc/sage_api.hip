@@ -54,6 +54,60 @@ size_t prep_scratch(int B, int H, int Lkv, int D) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
+// sage_quant_prep; skip_q leaves Q (q_i8, q_scale) to the main loop.
+int quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
+               int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, uint8_t* v_fp8,
+               float* v_scale, void* scratch, size_t scratch_bytes, int skip_q, void* stream) {
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  if (!q || !k || !v || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !v_fp8 || !v_scale || !scratch)
+    return SAGE_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(q_i8, 16) ||
+      misaligned(k_i8, 16) || misaligned(v_fp8, 16) || misaligned(q_scale, 4) || misaligned(k_scale, 4) ||
+      misaligned(k_mean, 16) || misaligned(v_scale, 16) || misaligned(scratch, 8))
+    return SAGE_ERR_INVALID_ARG;
+  if (scratch_bytes < prep_scratch(B, H, Lkv, D)) return SAGE_ERR_WORKSPACE;
+  const size_t n = (size_t)B * H * sage::prep_n_split(Lkv) * D;
+  sage::PrepArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.B = B; a.H = H; a.Lq = Lq; a.Lkv = Lkv; a.D = D;
+  a.nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
+  a.nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
+  a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale; a.k_mean = k_mean;
+  a.v_fp8 = v_fp8; a.v_scale = v_scale;
+  a.psum = (double*)scratch;
+  a.pmax = (float*)((char*)scratch + align_up(n * sizeof(double)));
+  a.skip_q = skip_q;
+  return hip_status(sage::launch_prep(a, (hipStream_t)stream));
+}
+
+
+// Validation and argument block shared by the main-loop entry points.
+int attn_args(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+              const uint8_t* v_fp8, const float* v_scale, void* out, int B, int H, int Lq, int Lkv, int D,
+              int causal, float sm_scale, sage::AttnArgs* a) {
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_fp8 || !v_scale || !out) return SAGE_ERR_INVALID_ARG;
+  if (misaligned(q_i8, 16) || misaligned(k_i8, 16) || misaligned(v_fp8, 16) || misaligned(out, 16) ||
+      misaligned(q_scale, 4) || misaligned(k_scale, 4) || misaligned(v_scale, 16))
+    return SAGE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
+  if (isnan(sm_scale) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
+  if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
+  *a = sage::AttnArgs{};
+  a->q_i8 = q_i8; a->q_scale = q_scale; a->k_i8 = k_i8; a->k_scale = k_scale;
+  a->v_fp8 = v_fp8; a->v_scale = v_scale; a->out = (uint16_t*)out;
+  a->B = B; a->H = H; a->Lq = Lq; a->Lkv = Lkv;
+  a->nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
+  a->nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
+  a->n_qtiles = (Lq + sage::kQTile - 1) / sage::kQTile;
+  a->scale_log2 = sm_scale * 1.4426950408889634f;
+  return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,61 +142,9 @@ int sage_workspace_bytes(int B, int H, int Lq, int Lkv, int D, size_t* bytes) {
 int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
                     uint8_t* v_fp8, float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
-  const int st = check_dims(B, H, Lq, Lkv, D);
-  if (st != SAGE_OK) return st;
-  if (!q || !k || !v || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !v_fp8 || !v_scale || !scratch)
-    return SAGE_ERR_INVALID_ARG;
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(q_i8, 16) ||
-      misaligned(k_i8, 16) || misaligned(v_fp8, 16) || misaligned(q_scale, 4) || misaligned(k_scale, 4) ||
-      misaligned(k_mean, 16) || misaligned(v_scale, 16) || misaligned(scratch, 8))
-    return SAGE_ERR_INVALID_ARG;
-  if (scratch_bytes < prep_scratch(B, H, Lkv, D)) return SAGE_ERR_WORKSPACE;
-  const size_t n = (size_t)B * H * sage::prep_n_split(Lkv) * D;
-  sage::PrepArgs a;
-  a.q = (const uint16_t*)q;
-  a.k = (const uint16_t*)k;
-  a.v = (const uint16_t*)v;
-  a.B = B; a.H = H; a.Lq = Lq; a.Lkv = Lkv; a.D = D;
-  a.nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
-  a.nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
-  a.q_i8 = q_i8; a.q_scale = q_scale; a.k_i8 = k_i8; a.k_scale = k_scale; a.k_mean = k_mean;
-  a.v_fp8 = v_fp8; a.v_scale = v_scale;
-  a.psum = (double*)scratch;
-  a.pmax = (float*)((char*)scratch + align_up(n * sizeof(double)));
-  return hip_status(sage::launch_prep(a, (hipStream_t)stream));
+  return quant_prep(q, k, v, B, H, Lq, Lkv, D, q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale, scratch,
+                    scratch_bytes, 0, stream);
 }
-
-}  // extern "C"
-
-namespace {
-
-// Validation and argument block shared by the main-loop entry points.
-int attn_args(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
-              const uint8_t* v_fp8, const float* v_scale, void* out, int B, int H, int Lq, int Lkv, int D,
-              int causal, float sm_scale, sage::AttnArgs* a) {
-  const int st = check_dims(B, H, Lq, Lkv, D);
-  if (st != SAGE_OK) return st;
-  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v_fp8 || !v_scale || !out) return SAGE_ERR_INVALID_ARG;
-  if (misaligned(q_i8, 16) || misaligned(k_i8, 16) || misaligned(v_fp8, 16) || misaligned(out, 16) ||
-      misaligned(q_scale, 4) || misaligned(k_scale, 4) || misaligned(v_scale, 16))
-    return SAGE_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
-  if (isnan(sm_scale) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
-  if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
-  *a = sage::AttnArgs{};
-  a->q_i8 = q_i8; a->q_scale = q_scale; a->k_i8 = k_i8; a->k_scale = k_scale;
-  a->v_fp8 = v_fp8; a->v_scale = v_scale; a->out = (uint16_t*)out;
-  a->B = B; a->H = H; a->Lq = Lq; a->Lkv = Lkv;
-  a->nqb = (Lq + sage::kBlock - 1) / sage::kBlock;
-  a->nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
-  a->n_qtiles = (Lq + sage::kQTile - 1) / sage::kQTile;
-  a->scale_log2 = sm_scale * 1.4426950408889634f;
-  return SAGE_OK;
-}
-
-}  // namespace
-
-extern "C" {
 
 int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
@@ -186,15 +188,20 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
   const Layout l = layout(B, H, Lq, Lkv, D);
   if (workspace_bytes < l.total) return SAGE_ERR_WORKSPACE;
   char* ws = (char*)workspace;
-  int s = sage_quant_prep(q, k, v, B, H, Lq, Lkv, D, (int8_t*)(ws + l.q_i8), (float*)(ws + l.q_scale),
-                          (int8_t*)(ws + l.k_i8), (float*)(ws + l.k_scale), (float*)(ws + l.k_mean),
-                          (uint8_t*)(ws + l.v_fp8), (float*)(ws + l.v_scale), ws + l.psum,
-                          l.total - l.psum, stream);
+  // K and V are prepared in the workspace; Q is quantized inside the main
+  // loop from bf16 (same codes and scales as sage_quant_prep would write).
+  int s = quant_prep(q, k, v, B, H, Lq, Lkv, D, (int8_t*)(ws + l.q_i8), (float*)(ws + l.q_scale),
+                     (int8_t*)(ws + l.k_i8), (float*)(ws + l.k_scale), (float*)(ws + l.k_mean),
+                     (uint8_t*)(ws + l.v_fp8), (float*)(ws + l.v_scale), ws + l.psum, l.total - l.psum, 1,
+                     stream);
   if (s != SAGE_OK) return s;
-  return sage_attn_fwd_prepped((const int8_t*)(ws + l.q_i8), (const float*)(ws + l.q_scale),
-                               (const int8_t*)(ws + l.k_i8), (const float*)(ws + l.k_scale),
-                               (const uint8_t*)(ws + l.v_fp8), (const float*)(ws + l.v_scale), out, B, H, Lq,
-                               Lkv, D, causal, sm_scale, stream);
+  sage::AttnArgs a;
+  s = attn_args((const int8_t*)(ws + l.q_i8), (const float*)(ws + l.q_scale), (const int8_t*)(ws + l.k_i8),
+                (const float*)(ws + l.k_scale), (const uint8_t*)(ws + l.v_fp8), (const float*)(ws + l.v_scale),
+                out, B, H, Lq, Lkv, D, causal, sm_scale, &a);
+  if (s != SAGE_OK) return s;
+  a.q_bf16 = (const uint16_t*)q;
+  return hip_status(sage::launch_attn_fused_q(a, D, causal == 1, (hipStream_t)stream));
 }
 
 int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int Lq, int Lkv, int D,

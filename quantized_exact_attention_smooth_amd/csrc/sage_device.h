@@ -24,6 +24,26 @@ __device__ __forceinline__ void unpack8(const uint4& u, float f[8]) {
   f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
 }
 
+// Correctly rounded x / s from r = RN(1 / s): q0 = RN(x r) is within an ulp
+// of x / s and the residual q0 s - x is exact in an fma, so one correction
+// step gives RN(x / s) (Markstein's theorem). The residual is formed as
+// q0 s - x so that x = -0 keeps its sign, as in a division. With
+// s >= 2^-60 the residual cannot underflow unless |x / s| < 2^-24, where
+// int8 and E4M3 codes are 0 whichever way the quotient rounds; below that
+// scale the caller divides. Shared by the preparation pass and the main
+// loop's fused Q quantization, so their codes agree bit for bit.
+constexpr float kFastDivMinScale = 0x1p-60f;
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  const float q0 = x * r;
+  return __builtin_fmaf(-__builtin_fmaf(q0, s, -x), r, q0);
+}
+
+// INT8 block code of a quotient already rounded to fp32: round half to even,
+// clamp to [-127, 127].
+__device__ __forceinline__ uint32_t code_i8(float q) {
+  return (uint32_t)(int)fminf(fmaxf(rintf(q), -127.0f), 127.0f) & 0xFFu;
+}
+
 // Byte offset of 16-byte chunk `chunk` of key row `key` in an LDS K tile of
 // 64 rows x D bytes. The XOR swizzle is linear in the key bits and was chosen
 // so that the A-operand reads of the QK step (16 bytes per lane) and the

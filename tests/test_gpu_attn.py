@@ -82,12 +82,32 @@ def test_ragged_and_edge_shapes(B, H, Lq, Lkv, D, causal, gpu_device):
             assert np.all(out[b, h, :Lq - Lkv] == 0)
 
 
+E2E_SHAPES = [(1, 1, 1, 1, 64, True), (1, 2, 63, 65, 128, False), (2, 1, 65, 1, 128, True),
+              (1, 3, 1000, 129, 64, True), (1, 1, 129, 1000, 128, True), (1, 2, 300, 300, 128, False),
+              (2, 2, 200, 511, 64, False)]
+
+
 def test_end_to_end_equals_prep_then_main(gpu_device):
+    # sage_attn_fwd codes Q inside the main loop; its codes and scales must be
+    # those sage_quant_prep writes, so the outputs agree bit for bit.
     w = si.WORKLOADS[1]
     q, k, v = si.workload_qkv(w)
     say("attn_fwd == quant_prep + attn_fwd_prepped")
     a = _gpu_out(q, k, v, True, w.sm_scale, gpu_device, end_to_end=True)
     b = _gpu_out(q, k, v, True, w.sm_scale, gpu_device)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("shape", E2E_SHAPES)
+def test_end_to_end_equals_prep_then_main_on_edges(shape, gpu_device):
+    B, H, Lq, Lkv, D, causal = shape
+    q, k, v = si.make_qkv(B, H, Lq, Lkv, D, "normal", 2.0, seed=31)
+    if Lq > 64:
+        q[:, :, 64:128] = 0  # an all-zero Q block (scale 0, codes 0)
+    say(f"attn_fwd == prep + prepped on {shape}")
+    sm = 1.0 / math.sqrt(D)
+    a = _gpu_out(q, k, v, causal, sm, gpu_device, end_to_end=True)
+    b = _gpu_out(q, k, v, causal, sm, gpu_device)
     assert np.array_equal(a, b)
 
 
