@@ -13,7 +13,8 @@
 //    the heads, so with B*H a multiple of 8 every tile of a head runs on the
 //    same XCD (blocks are dealt to the 8 XCDs round-robin) and shares its L2.
 //  * per 64-key epoch the K tile (64 x D int8) and V tile (D x 64 e4m3, keys
-//    contiguous) are staged in LDS, double-buffered through registers.
+//    contiguous) are copied straight from global memory into LDS (two slots
+//    each; K two epochs ahead, V one), no staging registers.
 //  * QK: S^T = K . Q^T with v_mfma_i32_32x32x32_i8 (A = K rows from LDS,
 //    B = Q codes held in registers for the whole kernel). The K rows are
 //    loaded in a permuted order so that each lane ends with 32 consecutive
@@ -25,9 +26,13 @@
 //  * P -> E4M3 in registers; that register block IS the B operand of the PV
 //    matrix-core step (O^T = V^T . P^T, v_mfma_f32_32x32x64_f8f6f4), so P
 //    never goes through LDS, and each lane's outputs belong to its own query.
-//  * two-level PV: the epoch's P.V is formed in fresh fp32 registers, then
-//    RO = RO * alpha + PV per element (one fma).
+//  * two-level PV: RO *= alpha (skipped when no row max of the wave moved,
+//    i.e. alpha == 1 in every lane), then the matrix core reduces the epoch's
+//    64 keys in fp32 (inner level) and adds the result into RO, its C
+//    operand (outer level).
 //  * epilogue: r = 1/l (IEEE divide), out = bf16(RO * r * sv[c]) for rows < Lq.
+//  * instantiations: QBF16 codes Q from bf16 inside the kernel (the
+//    end-to-end path); TRACE records one wave's per-epoch state (debug).
 #include <limits.h>
 
 #include <type_traits>
