@@ -6,7 +6,8 @@
 // quantization and FP8 V. The pass is bound by HBM bandwidth; three launches:
 //   stats    - one read of K and V: per (head, 256-row split) fp64 channel sums
 //              of K and fp32 channel absmax of V (16-byte coalesced loads);
-//   finalize - per head: mean = fp32(sum / Lkv), sv = absmax / 448;
+//   finalize - per head: mean = fp32(sum / Lkv), sv = absmax / 448 (the
+//              splits spread over the workgroup);
 //   quant    - one read of Q, K, V per 64-row block: block absmax, codes.
 // Every value is bit-identical to the definitions in sage_attn.h: the fp64
 // channel sum of bf16 inputs is exact (the sum of any subset is representable),
@@ -69,21 +70,50 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const uint16_t* __
   }
 }
 
+// Per head: mean = fp32(sum / Lkv) and sv = absmax / 448 from the split
+// partials. The kThreads / D thread groups of a channel each take every
+// G-th split with four loads in flight, then combine through LDS; the fp64
+// partial sums are exact, so the order does not matter.
 template <int D>
-__global__ __launch_bounds__(D) void prep_finalize_kernel(const double* __restrict__ psum,
-                                                          const float* __restrict__ pmax, int n_split,
-                                                          int Lkv, float* __restrict__ k_mean,
-                                                          float* __restrict__ v_scale) {
+__global__ __launch_bounds__(kThreads) void prep_finalize_kernel(const double* __restrict__ psum,
+                                                                 const float* __restrict__ pmax, int n_split,
+                                                                 int Lkv, float* __restrict__ k_mean,
+                                                                 float* __restrict__ v_scale) {
+  constexpr int G = kThreads / D;
+  __shared__ double s_sum[G][D];
+  __shared__ float s_max[G][D];
   const long bh = blockIdx.x;
-  const int c = threadIdx.x;
-  double a = 0.0;
-  float m = 0.0f;
-  for (int s = 0; s < n_split; ++s) {
-    a += psum[(bh * n_split + s) * D + c];
-    m = fmaxf(m, pmax[(bh * n_split + s) * D + c]);
+  const int c = threadIdx.x % D, g = threadIdx.x / D;
+  const double* ps = psum + bh * n_split * (long)D + c;
+  const float* pm = pmax + bh * n_split * (long)D + c;
+  double a[4] = {0.0, 0.0, 0.0, 0.0};
+  float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int s = g;
+  for (; s + 3 * G < n_split; s += 4 * G) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] += ps[(long)(s + u * G) * D];
+      m[u] = fmaxf(m[u], pm[(long)(s + u * G) * D]);
+    }
   }
-  k_mean[bh * D + c] = (float)(a / (double)Lkv);
-  v_scale[bh * D + c] = m / 448.0f;
+  for (; s < n_split; s += G) {
+    a[0] += ps[(long)s * D];
+    m[0] = fmaxf(m[0], pm[(long)s * D]);
+  }
+  s_sum[g][c] = (a[0] + a[1]) + (a[2] + a[3]);
+  s_max[g][c] = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+  __syncthreads();
+  if (g == 0) {
+    double t = 0.0;
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      t += s_sum[i][c];
+      mx = fmaxf(mx, s_max[i][c]);
+    }
+    k_mean[bh * D + c] = (float)(t / (double)Lkv);
+    v_scale[bh * D + c] = mx / 448.0f;
+  }
 }
 
 // Max over the workgroup of one float per thread (all threads get it).
@@ -251,14 +281,14 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
     prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    prep_finalize_kernel<128><<<g_fin, 128, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
+    prep_finalize_kernel<128><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     prep_quant_kernel<128><<<g_quant, kThreads, 0, stream>>>(a);
   } else {
     prep_stats_kernel<64><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    prep_finalize_kernel<64><<<g_fin, 64, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
+    prep_finalize_kernel<64><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     prep_quant_kernel<64><<<g_quant, kThreads, 0, stream>>>(a);
   }
