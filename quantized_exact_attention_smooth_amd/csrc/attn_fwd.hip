@@ -176,12 +176,13 @@ constexpr int kWaitLgkmOnly = 0xC07F;
 // Software pipeline per wave, one body per epoch e:
 //   1. start the LDS fills of K(e+2) and V(e+1) (buffers freed by the last
 //      barrier);
-//   2. QK matrix-core steps for epoch e+1 into the other accumulator set;
-//   3. softmax of epoch e (VALU) from the accumulators filled one body ago;
-//   4. RO *= alpha when some row's running max moved, then the PV step of
+//   2. softmax of epoch e (VALU) from the accumulators filled one body ago,
+//      with the QK matrix-core steps of epoch e+1 (into the other accumulator
+//      set) issued between groups of its exp2 evaluations;
+//   3. RO *= alpha when some row's running max moved, then the PV step of
 //      epoch e accumulates into RO inside the matrix core;
-//   5. wait for this body's LDS fills, barrier.
-// The QK results of step 2 and the PV results of step 4 are consumed one body
+//   4. wait for this body's LDS fills, barrier.
+// The QK results of step 2 and the PV results of step 3 are consumed one body
 // later, so neither matrix-core latency is exposed to the softmax.
 
 template <int D, bool CAUSAL, bool TRACE, bool QBF16>
@@ -317,8 +318,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
     uint8_t* v_fill = P ? s_v0 : s_v1;   // V(e+1) replaces V(e-1)
     if (e + 2 < n_ep) k_tile_to_lds<D>(kh + (long)(e + 2) * kBlock * D, k_fill, w, lane);
     if (e + 1 < n_ep) v_tile_to_lds<D>(vh + (long)(e + 1) * D * kBlock, v_fill, w, lane);
-    if (e + 1 < w_ep) qk_epoch<D>(k_next, qreg, lane, nxt0, nxt1);
     if (e < w_ep) {
+      // First K fragments of epoch e+1, read ahead of the row max.
+      const int key0 = qk_row_key(ql, 0), key1 = qk_row_key(ql, 1);
+      v4i kf[2][2];
+      kf[0][0] = *reinterpret_cast<const v4i*>(k_next + k_lds_off<D>(key0, h));
+      kf[0][1] = *reinterpret_cast<const v4i*>(k_next + k_lds_off<D>(key1, h));
+      __builtin_amdgcn_sched_barrier(0);
       // log2-domain score per unit of the int32 accumulator
       const float c = cq * ksh[e];
       int x[32];
@@ -348,9 +354,29 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(m - m_use);
       const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;  // wave-uniform
 
+      // p = exp2(S c - m), with the QK steps of epoch e+1 spread through it:
+      // each matrix-core step then runs while this wave keeps issuing VALU
+      // work, instead of stalling the wave on its dependent successor. On the
+      // wave's last epoch the steps read a stale K buffer and go unused.
+      constexpr int kSteps = 2 * (D / 32);     // MFMAs of one QK epoch
+      constexpr int kPer = 32 / kSteps;        // p values between two of them
       float p[32];
 #pragma unroll
-      for (int t = 0; t < 32; ++t) p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)x[t], c, -m_use));
+      for (int j = 0; j < kSteps; ++j) {
+        const int st = j >> 1;
+        if ((j & 1) == 0 && st + 1 < D / 32) {
+          kf[(st + 1) & 1][0] = *reinterpret_cast<const v4i*>(k_next + k_lds_off<D>(key0, 2 * (st + 1) + h));
+          kf[(st + 1) & 1][1] = *reinterpret_cast<const v4i*>(k_next + k_lds_off<D>(key1, 2 * (st + 1) + h));
+        }
+        if ((j & 1) == 0)
+          nxt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[st & 1][0], qreg[st], st ? nxt0 : v16i{}, 0, 0, 0);
+        else
+          nxt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[st & 1][1], qreg[st], st ? nxt1 : v16i{}, 0, 0, 0);
+#pragma unroll
+        for (int t = kPer * j; t < kPer * (j + 1); ++t)
+          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)x[t], c, -m_use));
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (masked) {
         asm volatile("" ::: "memory");
 #pragma unroll
@@ -438,7 +464,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 // ------------------------------------------------------------ debug kernels
 
 // One 64x64 int32 QK tile per workgroup (2 waves = 64 queries), through the
-// same staging and qk_epoch code as the main loop.
+// same staging and qk_epoch code as the main loop's first epoch (later epochs
+// interleave the same MFMA steps, same operands, with the softmax).
 template <int D>
 __global__ __launch_bounds__(128) void qk_debug_kernel(QkDebugArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBlock * D];
