@@ -44,12 +44,15 @@ MAIN_KERNEL_SOURCES = ("attn_fwd.hip", "sage_device.h", "sage_launch.h")
 
 
 def _src_hash() -> str:
-    """Hash of the main kernel's sources (the kernel the traffic counters describe)."""
+    """Hash of the main kernel's sources and compiler flags (the kernel the
+    traffic counters describe)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_exact_attention_smooth_amd", "csrc")
     for n in MAIN_KERNEL_SOURCES:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + f.read())
+    from quantized_exact_attention_smooth_amd.build import HIPCC_FLAGS
+    h.update(" ".join(f for f in HIPCC_FLAGS if not f.startswith("/")).encode())
     return h.hexdigest()[:16]
 
 
