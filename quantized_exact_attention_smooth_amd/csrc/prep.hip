@@ -17,6 +17,8 @@
 
 namespace sage {
 
+constexpr int kStatRows = 256;  // key rows per statistics workgroup (one split)
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, int Lkv,
@@ -36,20 +38,32 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const uint16_t* __
   const uint16_t* kh = k + bh * (long)Lkv * D;
   const uint16_t* vh = v + bh * (long)Lkv * D;
 
+  // Rows are taken kBatch at a time with every load of a batch issued first
+  // (rows past the end read as zero, which changes neither statistic).
+  constexpr int kBatch = 4;
+  static_assert(kStatRows % (kRowsPerIter * kBatch) == 0, "split is whole batches");
   double s[8];
   float mx[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) { s[i] = 0.0; mx[i] = 0.0f; }
-  for (int t = t0 + rg; t < t1; t += kRowsPerIter) {
-    uint4 uk = *reinterpret_cast<const uint4*>(kh + (long)t * D + 8 * cg);
-    uint4 uv = *reinterpret_cast<const uint4*>(vh + (long)t * D + 8 * cg);
-    float fk[8], fv[8];
-    unpack8(uk, fk);
-    unpack8(uv, fv);
+  for (int t = t0 + rg; t < t0 + kStatRows; t += kBatch * kRowsPerIter) {
+    uint4 uk[kBatch], uv[kBatch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s[i] += (double)fk[i];
-      mx[i] = fmaxf(mx[i], fabsf(fv[i]));
+    for (int u = 0; u < kBatch; ++u) {
+      const int r = t + u * kRowsPerIter;
+      uk[u] = r < t1 ? *reinterpret_cast<const uint4*>(kh + (long)r * D + 8 * cg) : make_uint4(0, 0, 0, 0);
+      uv[u] = r < t1 ? *reinterpret_cast<const uint4*>(vh + (long)r * D + 8 * cg) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      float fk[8], fv[8];
+      unpack8(uk[u], fk);
+      unpack8(uv[u], fv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s[i] += (double)fk[i];
+        mx[i] = fmaxf(mx[i], fabsf(fv[i]));
+      }
     }
   }
 #pragma unroll
@@ -128,23 +142,33 @@ __device__ __forceinline__ float block_max(float x, float* s_red) {
   return x;
 }
 
-// INT8 codes of one 64-row block of a [L][D] bf16 head (rows >= L are
-// padding: excluded from the absmax and coded 0). sub[c] is subtracted from
-// column c first (the K channel mean; nullptr for Q). Every load is issued
-// before the block reduction.
+// This thread's share of one 64-row block of a [L][D] bf16 head: 16-byte
+// chunks g = threadIdx.x + kThreads j, row g / (D / 8), columns 8 (g % (D / 8))
+// .. +7; rows >= L read as zero.
 template <int D>
-__device__ void quant_int8_block(const uint16_t* __restrict__ x, int L, int blk,
-                                 const float* __restrict__ sub, int8_t* __restrict__ codes,
-                                 float* __restrict__ scale, float* s_red) {
-  constexpr int kChunks = kBlock * D / 8 / kThreads;  // 8 values per chunk
-  constexpr int kLanesPerRow = D / 8;
+struct Int8BlockLoad {
+  static constexpr int kChunks = kBlock * D / 8 / kThreads;  // 8 values per chunk
+  static constexpr int kLanesPerRow = D / 8;
   uint4 raw[kChunks];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ x, int L, int blk) {
 #pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    const int g = threadIdx.x + kThreads * j;
-    const int row = blk * kBlock + g / kLanesPerRow, c0 = 8 * (g % kLanesPerRow);
-    raw[j] = (row < L) ? *reinterpret_cast<const uint4*>(x + (long)row * D + c0) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < kChunks; ++j) {
+      const int g = threadIdx.x + kThreads * j;
+      const int row = blk * kBlock + g / kLanesPerRow, c0 = 8 * (g % kLanesPerRow);
+      raw[j] = (row < L) ? *reinterpret_cast<const uint4*>(x + (long)row * D + c0) : make_uint4(0, 0, 0, 0);
+    }
   }
+};
+
+// INT8 codes of one loaded 64-row block (rows >= L are padding: excluded from
+// the absmax and coded 0). sub[c] is subtracted from column c first (the K
+// channel mean; nullptr for Q).
+template <int D>
+__device__ void quant_int8_block(const Int8BlockLoad<D>& ld, int L, int blk, const float* __restrict__ sub,
+                                 int8_t* __restrict__ codes, float* __restrict__ scale, float* s_red) {
+  constexpr int kChunks = Int8BlockLoad<D>::kChunks;
+  constexpr int kLanesPerRow = Int8BlockLoad<D>::kLanesPerRow;
+  const uint4* raw = ld.raw;
   float f[kChunks][8];
   float a = 0.0f;
 #pragma unroll
@@ -193,21 +217,36 @@ __device__ void quant_int8_block(const uint16_t* __restrict__ x, int L, int blk,
 // division when some scale of the head is tiny) and then converted by the
 // hardware E4M3 conversion (nearest even; |v / sv| <= 448 up to rounding).
 template <int D>
-__device__ void quant_v_block(const uint16_t* __restrict__ v, int L, int blk, const float* __restrict__ sv,
+struct VBlockLoad {
+  static constexpr int kUnits = (kBlock / 4) * (D / 8);
+  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+  uint4 raw[kPerThread][4];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ v, int L, int blk) {
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int u = threadIdx.x + kThreads * k;
+      if (u >= kUnits) break;
+      const int kq = u % (kBlock / 4), c0 = 8 * (u / (kBlock / 4));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = blk * kBlock + 4 * kq + r;
+        raw[k][r] = (row < L) ? *reinterpret_cast<const uint4*>(v + (long)row * D + c0) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <int D>
+__device__ void quant_v_block(const VBlockLoad<D>& ld, int L, int blk, const float* __restrict__ sv,
                               const float* __restrict__ rv, bool fast, uint8_t* __restrict__ tile,
                               uint8_t* s_tile) {
-  constexpr int kUnits = (kBlock / 4) * (D / 8);
+  constexpr int kUnits = VBlockLoad<D>::kUnits;
 #pragma unroll
-  for (int k = 0; k < (kUnits + kThreads - 1) / kThreads; ++k) {
+  for (int k = 0; k < VBlockLoad<D>::kPerThread; ++k) {
     const int u = threadIdx.x + kThreads * k;
     if (u >= kUnits) break;
     const int kq = u % (kBlock / 4), c0 = 8 * (u / (kBlock / 4));
-    uint4 raw[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = blk * kBlock + 4 * kq + r;
-      raw[r] = (row < L) ? *reinterpret_cast<const uint4*>(v + (long)row * D + c0) : make_uint4(0, 0, 0, 0);
-    }
+    const uint4* raw = ld.raw[k];
     float f[4][8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) unpack8(raw[r], f[r]);
@@ -247,17 +286,25 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
   __shared__ float s_rv[D];  // RN(1 / V channel scale)
   const int job = blockIdx.x + (a.skip_q ? a.nqb : 0);
   const long bh = blockIdx.y;
+  // The block's data loads are issued before the per-head channel values are
+  // read, so the two memory latencies overlap.
   if (job < a.nqb) {
-    quant_int8_block<D>(a.q + bh * (long)a.Lq * D, a.Lq, job, nullptr,
-                        a.q_i8 + bh * (long)a.nqb * kBlock * D, a.q_scale + bh * a.nqb + job, s_red);
+    Int8BlockLoad<D> ld;
+    ld.load(a.q + bh * (long)a.Lq * D, a.Lq, job);
+    quant_int8_block<D>(ld, a.Lq, job, nullptr, a.q_i8 + bh * (long)a.nqb * kBlock * D,
+                        a.q_scale + bh * a.nqb + job, s_red);
   } else if (job < a.nqb + a.nkb) {
     const int blk = job - a.nqb;
+    Int8BlockLoad<D> ld;
+    ld.load(a.k + bh * (long)a.Lkv * D, a.Lkv, blk);
     if (threadIdx.x < D) s_ch[threadIdx.x] = a.k_mean[bh * D + threadIdx.x];
     __syncthreads();
-    quant_int8_block<D>(a.k + bh * (long)a.Lkv * D, a.Lkv, blk, s_ch,
-                        a.k_i8 + bh * (long)a.nkb * kBlock * D, a.k_scale + bh * a.nkb + blk, s_red);
+    quant_int8_block<D>(ld, a.Lkv, blk, s_ch, a.k_i8 + bh * (long)a.nkb * kBlock * D,
+                        a.k_scale + bh * a.nkb + blk, s_red);
   } else {
     const int blk = job - a.nqb - a.nkb;
+    VBlockLoad<D> ld;
+    ld.load(a.v + bh * (long)a.Lkv * D, a.Lkv, blk);
     bool tiny = false;
     if (threadIdx.x < D) {
       const float s = a.v_scale[bh * D + threadIdx.x];
@@ -266,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
       s_rv[threadIdx.x] = tiny || s == 0.0f ? 0.0f : 1.0f / s;
     }
     const bool fast = !__syncthreads_or(tiny);
-    quant_v_block<D>(a.v + bh * (long)a.Lkv * D, a.Lkv, blk, s_ch, s_rv, fast,
+    quant_v_block<D>(ld, a.Lkv, blk, s_ch, s_rv, fast,
                      a.v_fp8 + (bh * a.nkb + blk) * (long)D * kBlock, s_tile);
   }
 }

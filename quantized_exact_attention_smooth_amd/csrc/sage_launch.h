@@ -9,7 +9,6 @@ namespace sage {
 constexpr int kBlock = 64;      // quant block rows == attention epoch keys
 constexpr int kThreads = 256;   // 4 wave64 per workgroup
 constexpr int kQTile = 128;     // query rows per main-loop workgroup (32 per wave)
-constexpr int kStatRows = 256;  // key rows per preparation statistics workgroup
 
 struct PrepArgs {
   const uint16_t* q;
