@@ -1,9 +1,9 @@
 """Throughput of the quantized attention path on one MI355X.
 
 One step = the whole path on one batch: sage_attn_fwd, the user-facing call
-(K mean, smoothing, INT8 K blocks and FP8 V in the preparation pass, then
-the fused main loop, which quantizes Q itself), on inputs already resident
-in HBM. Prints one JSON line.
+(K mean, smoothing, INT8 Q and K blocks and FP8 V in the preparation pass,
+then the fused main loop), on inputs already resident in HBM. Prints one
+JSON line.
 
   value     whole-step throughput in TOPS, ops = 4*B*H*Lq*Lkv*D (halved when
             causal), over the wall time of K steps between two device syncs;

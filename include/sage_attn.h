@@ -102,12 +102,10 @@ int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t
                           int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, void* stream);
 
 /*
- * The whole path: K and V are prepared into the workspace as
- * sage_quant_prep would, and the main loop quantizes Q itself from the bf16
- * input (the same codes and scales, so the output equals sage_quant_prep
- * followed by sage_attn_fwd_prepped bit for bit; the workspace's q_i8 and
- * q_scale parts are not written). workspace: device memory of at least
- * sage_workspace_bytes, 256-byte aligned; it is overwritten.
+ * The whole path: sage_quant_prep into the workspace (its parts laid out as
+ * sage_workspace_bytes describes), then sage_attn_fwd_prepped on them, both
+ * on stream. workspace: device memory of at least sage_workspace_bytes,
+ * 256-byte aligned; it is overwritten.
  */
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
                   int D, int causal, float sm_scale, void* workspace, size_t workspace_bytes,

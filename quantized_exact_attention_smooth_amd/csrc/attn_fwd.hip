@@ -31,8 +31,7 @@
 //    64 keys in fp32 (inner level) and adds the result into RO, its C
 //    operand (outer level).
 //  * epilogue: r = 1/l (IEEE divide), out = bf16(RO * r * sv[c]) for rows < Lq.
-//  * instantiations: QBF16 codes Q from bf16 inside the kernel (the
-//    end-to-end path); TRACE records one wave's per-epoch state (debug).
+//  * instantiations: TRACE records one wave's per-epoch state (debug).
 #include <limits.h>
 
 #include <type_traits>
@@ -187,7 +186,7 @@ constexpr int kWaitLgkmOnly = 0xC07F;
 // and its result is consumed one body later. After the last body the PV step
 // of the wave's final epoch completes RO.
 
-template <int D, bool CAUSAL, bool TRACE, bool QBF16>
+template <int D, bool CAUSAL, bool TRACE>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   // Four separate LDS objects (not one array) so that the compiler can tell
   // the in-flight direct fills apart from the buffers being read.
@@ -237,63 +236,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   }
 
   v4i qreg[D / 32];
-  float sq;
-  if constexpr (QBF16) {
-    // Q quantized here from bf16, as the preparation pass would: this lane
-    // codes row qrow, columns 32s + 16h .. +15; the 64-row block's scale is
-    // the absmax over the two waves that own the block (rows >= Lq count 0
-    // and code 0).
-    __shared__ float s_qmax[kThreads / 64];
-    float f[D / 32][16];
-    float am = 0.0f;
-    const uint16_t* qsrc = a.q_bf16 + (bh * a.Lq + qrow) * (long)D;
+  const int8_t* qh = a.q_i8 + bh * (long)a.nqb * kBlock * D;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      uint4 u0 = make_uint4(0u, 0u, 0u, 0u), u1 = u0;
-      if (qrow < a.Lq) {
-        u0 = *reinterpret_cast<const uint4*>(qsrc + 32 * s + 16 * h);
-        u1 = *reinterpret_cast<const uint4*>(qsrc + 32 * s + 16 * h + 8);
-      }
-      unpack8(u0, f[s]);
-      unpack8(u1, f[s] + 8);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(f[s][j]));
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-    if (lane == 0) s_qmax[w] = am;
-    // LDS exchange only: wait for this wave's LDS write, not for the K/V
-    // fills in flight.
-    __builtin_amdgcn_s_waitcnt(kWaitLgkmOnly);
-    asm volatile("s_barrier" ::: "memory");
-    const float qa = fmaxf(s_qmax[w & ~1], s_qmax[w | 1]);
-    const float s_q = qa / 127.0f;
-    const bool fast = s_q >= kFastDivMinScale;
-    const float rq = fast ? 1.0f / s_q : 0.0f;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t word = 0u;
-        if (qa != 0.0f) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = f[s][4 * d + j];
-            word |= code_i8(fast ? div_rn(x, s_q, rq) : x / s_q) << (8 * j);
-          }
-        }
-        qreg[s][d] = (int)word;
-      }
-    }
-    sq = wave_on ? s_q : 0.0f;
-  } else {
-    const int8_t* qh = a.q_i8 + bh * (long)a.nqb * kBlock * D;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      qreg[s] = (qrow < a.Lq) ? *reinterpret_cast<const v4i*>(qh + (long)qrow * D + 32 * s + 16 * h)
-                              : v4i{};
-    sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
-  }
+  for (int s = 0; s < D / 32; ++s)
+    qreg[s] = (qrow < a.Lq) ? *reinterpret_cast<const v4i*>(qh + (long)qrow * D + 32 * s + 16 * h) : v4i{};
+  const float sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
   const float cq = sq * a.scale_log2;
 
   float m = -INFINITY, l = 0.0f;
@@ -559,28 +506,24 @@ __global__ __launch_bounds__(256) void codecs_debug_kernel(const float* __restri
 
 // ------------------------------------------------------------ launchers
 
-template <int D, bool C, bool T, bool QB>
+template <int D, bool C, bool T>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   const long blocks = T ? 1L : (long)a.n_qtiles * a.B * a.H;
-  attn_fwd_kernel<D, C, T, QB><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
+  attn_fwd_kernel<D, C, T><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <bool T, bool QB>
+template <bool T>
 static hipError_t launch_attn_v(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  if (D == 128)
-    return causal ? launch_attn_t<128, true, T, QB>(a, stream) : launch_attn_t<128, false, T, QB>(a, stream);
-  return causal ? launch_attn_t<64, true, T, QB>(a, stream) : launch_attn_t<64, false, T, QB>(a, stream);
+  if (D == 128) return causal ? launch_attn_t<128, true, T>(a, stream) : launch_attn_t<128, false, T>(a, stream);
+  return causal ? launch_attn_t<64, true, T>(a, stream) : launch_attn_t<64, false, T>(a, stream);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  return launch_attn_v<false, false>(a, D, causal, stream);
+  return launch_attn_v<false>(a, D, causal, stream);
 }
 hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  return launch_attn_v<true, false>(a, D, causal, stream);
-}
-hipError_t launch_attn_fused_q(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  return launch_attn_v<false, true>(a, D, causal, stream);
+  return launch_attn_v<true>(a, D, causal, stream);
 }
 
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream) {

@@ -276,15 +276,14 @@ __device__ void quant_v_block(const VBlockLoad<D>& ld, int L, int blk, const flo
 }
 
 // One workgroup per (tensor, 64-row block): job in [0, nqb) codes a Q block,
-// [nqb, nqb + nkb) a K block, [nqb + nkb, nqb + 2 nkb) a V block. With
-// a.skip_q the grid covers the K and V jobs only.
+// [nqb, nqb + nkb) a K block, [nqb + nkb, nqb + 2 nkb) a V block.
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
   __shared__ float s_red[4];
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[D * kBlock];
   __shared__ float s_ch[D];  // K channel mean, or V channel scale
   __shared__ float s_rv[D];  // RN(1 / V channel scale)
-  const int job = blockIdx.x + (a.skip_q ? a.nqb : 0);
+  const int job = blockIdx.x;
   const long bh = blockIdx.y;
   // The block's data loads are issued before the per-head channel values are
   // read, so the two memory latencies overlap.
@@ -323,7 +322,7 @@ int prep_n_split(int Lkv) { return (Lkv + kStatRows - 1) / kStatRows; }
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   const int ns = prep_n_split(a.Lkv);
-  const dim3 g_stats(ns, BH), g_fin(BH), g_quant((a.skip_q ? 0 : a.nqb) + 2 * a.nkb, BH);
+  const dim3 g_stats(ns, BH), g_fin(BH), g_quant(a.nqb + 2 * a.nkb, BH);
   if (a.D == 128) {
     prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();

@@ -54,10 +54,10 @@ size_t prep_scratch(int B, int H, int Lkv, int D) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
-// sage_quant_prep; skip_q leaves Q (q_i8, q_scale) to the main loop.
+// sage_quant_prep.
 int quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
                int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, uint8_t* v_fp8,
-               float* v_scale, void* scratch, size_t scratch_bytes, int skip_q, void* stream) {
+               float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
   const int st = check_dims(B, H, Lq, Lkv, D);
   if (st != SAGE_OK) return st;
   if (!q || !k || !v || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !v_fp8 || !v_scale || !scratch)
@@ -79,7 +79,6 @@ int quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq
   a.v_fp8 = v_fp8; a.v_scale = v_scale;
   a.psum = (double*)scratch;
   a.pmax = (float*)((char*)scratch + align_up(n * sizeof(double)));
-  a.skip_q = skip_q;
   return hip_status(sage::launch_prep(a, (hipStream_t)stream));
 }
 
@@ -143,7 +142,7 @@ int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, i
                     int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
                     uint8_t* v_fp8, float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
   return quant_prep(q, k, v, B, H, Lq, Lkv, D, q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale, scratch,
-                    scratch_bytes, 0, stream);
+                    scratch_bytes, stream);
 }
 
 int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
@@ -188,20 +187,18 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
   const Layout l = layout(B, H, Lq, Lkv, D);
   if (workspace_bytes < l.total) return SAGE_ERR_WORKSPACE;
   char* ws = (char*)workspace;
-  // K and V are prepared in the workspace; Q is quantized inside the main
-  // loop from bf16 (same codes and scales as sage_quant_prep would write).
+  // The preparation pass writes every operand into the workspace, then the
+  // main loop runs on them.
   int s = quant_prep(q, k, v, B, H, Lq, Lkv, D, (int8_t*)(ws + l.q_i8), (float*)(ws + l.q_scale),
                      (int8_t*)(ws + l.k_i8), (float*)(ws + l.k_scale), (float*)(ws + l.k_mean),
-                     (uint8_t*)(ws + l.v_fp8), (float*)(ws + l.v_scale), ws + l.psum, l.total - l.psum, 1,
-                     stream);
+                     (uint8_t*)(ws + l.v_fp8), (float*)(ws + l.v_scale), ws + l.psum, l.total - l.psum, stream);
   if (s != SAGE_OK) return s;
   sage::AttnArgs a;
   s = attn_args((const int8_t*)(ws + l.q_i8), (const float*)(ws + l.q_scale), (const int8_t*)(ws + l.k_i8),
                 (const float*)(ws + l.k_scale), (const uint8_t*)(ws + l.v_fp8), (const float*)(ws + l.v_scale),
                 out, B, H, Lq, Lkv, D, causal, sm_scale, &a);
   if (s != SAGE_OK) return s;
-  a.q_bf16 = (const uint16_t*)q;
-  return hip_status(sage::launch_attn_fused_q(a, D, causal == 1, (hipStream_t)stream));
+  return hip_status(sage::launch_attn(a, D, causal == 1, (hipStream_t)stream));
 }
 
 int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int Lq, int Lkv, int D,

@@ -30,8 +30,7 @@ __device__ __forceinline__ void unpack8(const uint4& u, float f[8]) {
 // q0 s - x so that x = -0 keeps its sign, as in a division. With
 // s >= 2^-60 the residual cannot underflow unless |x / s| < 2^-24, where
 // int8 and E4M3 codes are 0 whichever way the quotient rounds; below that
-// scale the caller divides. Shared by the preparation pass and the main
-// loop's fused Q quantization, so their codes agree bit for bit.
+// scale the caller divides.
 constexpr float kFastDivMinScale = 0x1p-60f;
 __device__ __forceinline__ float div_rn(float x, float s, float r) {
   const float q0 = x * r;

@@ -24,7 +24,6 @@ struct PrepArgs {
   float* v_scale;
   double* psum;  // [B*H][n_split][D] fp64 channel partial sums of K
   float* pmax;   // [B*H][n_split][D] channel absmax partials of V
-  int skip_q;    // 1: leave Q to the main loop (codes K and V only)
 };
 
 struct AttnArgs {
@@ -40,7 +39,6 @@ struct AttnArgs {
   // Per-epoch checkpoints (trace launches only): the workgroup runs tile
   // trace_tile of head trace_bh, and wave trace_wave writes its 32 rows'
   // state after every epoch (layouts in sage_attn.h).
-  const uint16_t* q_bf16;  // fused-Q launches: raw bf16 Q [B][H][Lq][D] (q_i8, q_scale unused)
   int trace_bh, trace_tile, trace_wave;
   float* tr_stats;
   uint8_t* tr_p8;
@@ -60,7 +58,6 @@ int prep_n_split(int Lkv);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, hipStream_t stream);
-hipError_t launch_attn_fused_q(const AttnArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream);
 hipError_t launch_codecs_debug(const float* x, int n, uint8_t* p8, uint16_t* bf16, hipStream_t stream);
 

@@ -88,8 +88,8 @@ E2E_SHAPES = [(1, 1, 1, 1, 64, True), (1, 2, 63, 65, 128, False), (2, 1, 65, 1, 
 
 
 def test_end_to_end_equals_prep_then_main(gpu_device):
-    # sage_attn_fwd codes Q inside the main loop; its codes and scales must be
-    # those sage_quant_prep writes, so the outputs agree bit for bit.
+    # sage_attn_fwd runs the preparation pass into its workspace and then the
+    # main loop: the output equals the two public calls bit for bit.
     w = si.WORKLOADS[1]
     q, k, v = si.workload_qkv(w)
     say("attn_fwd == quant_prep + attn_fwd_prepped")
