@@ -126,11 +126,19 @@ __device__ __forceinline__ uint32_t pack2_bf16(float x0, float x1) {
   return (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
 }
 
-// Direct global -> LDS copies (no staging registers). A wave copies 64
-// consecutive 16-byte LDS chunks per instruction; each lane fetches the global
-// chunk that the swizzled layout places at its LDS position.
+// Direct global -> LDS copies (no staging registers) through buffer loads:
+// a wave copies 64 consecutive 16-byte LDS chunks per instruction; each lane
+// fetches the global chunk that the swizzled layout places at its LDS
+// position. In the buffer form (rather than global_load_lds) the per-lane
+// offsets stay loop-invariant and the tile offset is a scalar, so a fill
+// costs no per-epoch address arithmetic, and the compiler can wait for the
+// main loop's LDS reads one by one while copies are in flight. rsrc spans one
+// head's tiles; tile is the byte offset of the tile in it.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int kRawBufferFlags = 0x00020000;  // untyped 32-bit access
 template <int D>
-__device__ __forceinline__ void k_tile_to_lds(const int8_t* __restrict__ src, uint8_t* lds, int w, int lane) {
+__device__ __forceinline__ void k_tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int tile, uint8_t* lds, int w,
+                                              int lane) {
   constexpr int kPerWave = kBlock * D / 16 / 4 / 64;  // instructions per wave
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
@@ -138,11 +146,12 @@ __device__ __forceinline__ void k_tile_to_lds(const int8_t* __restrict__ src, ui
     const int p = p0 + lane;
     const int key = p / (D / 16), pc = p % (D / 16);
     const int c = (k_lds_off<D>(key, pc) - key * D) >> 4;  // logical chunk at physical pc
-    __builtin_amdgcn_global_load_lds(src + key * D + 16 * c, lds + 16 * p0, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + 16 * p0), 16, key * D + 16 * c, tile, 0, 0);
   }
 }
 template <int D>
-__device__ __forceinline__ void v_tile_to_lds(const uint8_t* __restrict__ src, uint8_t* lds, int w, int lane) {
+__device__ __forceinline__ void v_tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int tile, uint8_t* lds, int w,
+                                              int lane) {
   constexpr int kPerWave = D * kBlock / 16 / 4 / 64;
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
@@ -150,7 +159,7 @@ __device__ __forceinline__ void v_tile_to_lds(const uint8_t* __restrict__ src, u
     const int p = p0 + lane;
     const int row = p / 4, pc = p % 4;
     const int c = (v_lds_off(row, pc) - row * 64) >> 4;
-    __builtin_amdgcn_global_load_lds(src + row * 64 + 16 * c, lds + 16 * p0, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + 16 * p0), 16, row * 64 + 16 * c, tile, 0, 0);
   }
 }
 
@@ -225,14 +234,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 
   // The first K/V fills start before the Q codes are set up, so that their
   // latency overlaps the Q loads.
-  const int8_t* kh = a.k_i8 + bh * (long)a.nkb * kBlock * D;
-  const uint8_t* vh = a.v_fp8 + bh * (long)a.nkb * D * kBlock;
+  // Buffer resources over this head's K and V tiles (the host bounds a head's
+  // tiles below 2^31 bytes, so offsets and the record count fit).
+  const int head_bytes = a.nkb * kBlock * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k_i8 + bh * (long)head_bytes), (short)0, head_bytes, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.v_fp8 + bh * (long)head_bytes), (short)0, head_bytes, kRawBufferFlags);
   // k_scale is read-only for the kernel's lifetime: scalar (constant-space) loads.
   const __attribute__((address_space(4))) float* ksh =
       (const __attribute__((address_space(4))) float*)(a.k_scale + bh * a.nkb);
   if (n_ep > 0) {
-    k_tile_to_lds<D>(kh, s_k0, w, lane);
-    if (n_ep > 1) k_tile_to_lds<D>(kh + kBlock * D, s_k1, w, lane);
+    k_tile_to_lds<D>(krs, 0, s_k0, w, lane);
+    if (n_ep > 1) k_tile_to_lds<D>(krs, kBlock * D, s_k1, w, lane);
   }
 
   v4i qreg[D / 32];
@@ -296,8 +310,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
     uint8_t* k_next = P ? s_k0 : s_k1;   // K(e+1)
     uint8_t* v_prev = P ? s_v0 : s_v1;   // V(e-1)
     uint8_t* v_fill = P ? s_v1 : s_v0;   // V(e) replaces V(e-2)
-    if (e + 2 < n_ep) k_tile_to_lds<D>(kh + (long)(e + 2) * kBlock * D, k_fill, w, lane);
-    v_tile_to_lds<D>(vh + (long)e * D * kBlock, v_fill, w, lane);
+    if (e + 2 < n_ep) k_tile_to_lds<D>(krs, (e + 2) * kBlock * D, k_fill, w, lane);
+    v_tile_to_lds<D>(vrs, e * D * kBlock, v_fill, w, lane);
     // A wave whose last epoch was e-1 (the workgroup stages more for the
     // other waves) runs one more body: every key of epoch e is past each of
     // its rows' limits, so p = 0, alpha = 1 and m, l stay, and the body only

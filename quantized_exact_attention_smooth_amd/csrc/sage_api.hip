@@ -21,6 +21,9 @@ int check_dims(int B, int H, int Lq, int Lkv, int D) {
   if (elems >= 1099511627776.0) return SAGE_ERR_INVALID_ARG;  // 2^40
   const double qtiles = (double)B * H * ((Lq + sage::kQTile - 1) / sage::kQTile);
   if (qtiles >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
+  // The main loop addresses one head's K or V codes with 32-bit buffer offsets.
+  const double head_codes = (double)((Lkv + sage::kBlock - 1) / sage::kBlock) * sage::kBlock * D;
+  if (head_codes >= 2147483648.0) return SAGE_ERR_INVALID_ARG;
   return SAGE_OK;
 }
 

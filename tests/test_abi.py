@@ -65,6 +65,10 @@ def test_size_queries_validate_shapes(lib):
     assert _ws(lib, 1, 1, 64, 64, 96)[0] == -2
     assert _ws(lib, 1, 1, 64, 64, 256)[0] == -2
     assert _ws(lib, 1 << 20, 1 << 10, 1 << 12, 1 << 12, 128)[0] == -1  # overflow guard
+    # one head's K codes must stay below 2 GiB (32-bit buffer offsets)
+    assert _ws(lib, 1, 1, 64, (1 << 24) - 64, 128)[0] == 0
+    assert _ws(lib, 1, 1, 64, (1 << 24) - 63, 128)[0] == -1
+    assert _ws(lib, 1, 1, 64, 1 << 25, 64)[0] == -1
     assert lib.sage_workspace_bytes(1, 1, 64, 64, 64, None) == -1
 
 
