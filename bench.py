@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -43,14 +44,22 @@ HBM_PEAK_GBS = 8000.0
 MAIN_KERNEL_SOURCES = ("attn_fwd.hip", "sage_device.h", "sage_launch.h")
 
 
+def _code_text(src: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that a
+    comment edit does not count as a kernel change."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def _src_hash() -> str:
-    """Hash of the main kernel's sources and compiler flags (the kernel the
-    traffic counters describe)."""
+    """Hash of the main kernel's code (sources without comments) and compiler
+    flags: the kernel the traffic counters describe."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_exact_attention_smooth_amd", "csrc")
     for n in MAIN_KERNEL_SOURCES:
-        with open(os.path.join(csrc, n), "rb") as f:
-            h.update(n.encode() + f.read())
+        with open(os.path.join(csrc, n), encoding="utf-8") as f:
+            h.update(n.encode() + _code_text(f.read()).encode())
     from quantized_exact_attention_smooth_amd.build import HIPCC_FLAGS
     h.update(" ".join(f for f in HIPCC_FLAGS if not f.startswith("/")).encode())
     return h.hexdigest()[:16]

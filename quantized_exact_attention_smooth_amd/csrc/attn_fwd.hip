@@ -232,8 +232,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   const int lim = CAUSAL ? min(qrow + off, a.Lkv - 1) : a.Lkv - 1;
   const int w_lim = CAUSAL ? min(wrow0 + off, a.Lkv - 1) : a.Lkv - 1;
 
-  // The first K/V fills start before the Q codes are set up, so that their
-  // latency overlaps the Q loads.
   // Buffer resources over this head's K and V tiles (the host bounds a head's
   // tiles below 2^31 bytes, so offsets and the record count fit).
   const int head_bytes = a.nkb * kBlock * D;
@@ -244,6 +242,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   // k_scale is read-only for the kernel's lifetime: scalar (constant-space) loads.
   const __attribute__((address_space(4))) float* ksh =
       (const __attribute__((address_space(4))) float*)(a.k_scale + bh * a.nkb);
+  // The first two K fills start before the Q codes are loaded, so that the
+  // latencies overlap (V(0) is filled by the first body).
   if (n_ep > 0) {
     k_tile_to_lds<D>(krs, 0, s_k0, w, lane);
     if (n_ep > 1) k_tile_to_lds<D>(krs, kBlock * D, s_k1, w, lane);
