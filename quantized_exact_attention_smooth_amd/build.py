@@ -18,10 +18,10 @@ SOURCES = ["prep.hip", "attn_fwd.hip", "sage_api.hip"]
 # -packed-fp32-ops off: no packed fp32 VALU instructions are generated.
 # -amdgpu-mfma-vgpr-form: matrix-core results land in VGPRs, which the
 # softmax and RO update read directly (no AGPR-to-VGPR copies).
-# -disable-machine-sink: the main loop places its matrix-core steps between
-# groups of softmax instructions (sched_barrier fences); machine sinking would
-# move the PV steps down to their first use after the mask branch, bunching
-# them up and raising register use past the two-waves-per-SIMD limit.
+# -disable-machine-sink: machine sinking moves values down to their first use
+# past the main loop's mask branches and so keeps more of them live at once;
+# with it the main loop no longer fits its register budget (168 VGPRs for
+# three waves per SIMD at D = 128) and spills.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-disable-machine-sink",

@@ -12,9 +12,14 @@
 //    Grid order puts the heaviest causal tiles first; consecutive blocks walk
 //    the heads, so with B*H a multiple of 8 every tile of a head runs on the
 //    same XCD (blocks are dealt to the 8 XCDs round-robin) and shares its L2.
+//  * three workgroups per CU at D = 128 (four at D = 64): the loop keeps one
+//    set of score registers and packs P as it is produced, so it fits 168
+//    VGPRs and each SIMD holds three waves (four at D = 64), which cover each
+//    other's matrix-core steps and stalls.
 //  * per 64-key epoch the K tile (64 x D int8) and V tile (D x 64 e4m3, keys
 //    contiguous) are copied straight from global memory into LDS (two slots
-//    each; K(e+2) and V(e) fill while epoch e computes), no staging registers.
+//    each; K(e+1) and V(e+1) fill while epoch e computes), no staging
+//    registers.
 //  * QK: S^T = K . Q^T with v_mfma_i32_32x32x32_i8 (A = K rows from LDS,
 //    B = Q codes held in registers for the whole kernel). The K rows are
 //    loaded in a permuted order so that each lane ends with 32 consecutive
@@ -181,22 +186,27 @@ constexpr int kWaitLgkmOnly = 0xC07F;
 
 // ------------------------------------------------------------ main kernel
 //
-// Software pipeline per wave, one body per epoch e:
-//   1. start the LDS fills of K(e+2) and V(e) (buffers freed by the last
+// Per wave, one body per epoch e:
+//   1. start the LDS fills of K(e+1) and V(e+1) (buffers freed by the last
 //      barrier);
-//   2. softmax of epoch e (VALU) from the accumulators filled one body ago;
-//      between groups of its exp2 evaluations the wave issues the QK
-//      matrix-core steps of epoch e+1 (into the other accumulator set) and
-//      the PV steps of epoch e-1 (RO += V(e-1)^T . P(e-1)^T);
-//   3. RO *= alpha(e) when some row's running max moved (RO now holds the
-//      epochs before e, exactly as in an undeferred order);
-//   4. wait for this body's LDS fills, barrier.
-// Every matrix-core step thus runs while the wave keeps issuing softmax work,
-// and its result is consumed one body later. After the last body the PV step
-// of the wave's final epoch completes RO.
+//   2. QK matrix-core steps of epoch e from the resident K(e);
+//   3. softmax of epoch e (VALU): row max, alpha, then p in groups of four
+//      keys, each group packed to E4M3 and added to the row sum at once;
+//   4. RO *= alpha when some row's running max moved, then the PV step of
+//      epoch e into RO;
+//   5. wait for this body's LDS fills, barrier.
+// A wave stalls on its own matrix-core steps; the other waves of the SIMD
+// issue VALU work meanwhile.
+
+// Waves per SIMD the register budget is set for: 3 at D = 128 (<= 168
+// VGPRs), 4 at D = 64 (<= 128); the trace build stores extra state and runs
+// one workgroup, so it keeps the compiler's default.
+template <int D, bool TRACE>
+constexpr int kWavesPerSimd = TRACE ? 1 : (D == 64 ? 4 : 3);
 
 template <int D, bool CAUSAL, bool TRACE>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, TRACE>)))
+void attn_fwd_kernel(AttnArgs a) {
   // Four separate LDS objects (not one array) so that the compiler can tell
   // the in-flight direct fills apart from the buffers being read.
   __shared__ __attribute__((aligned(16))) uint8_t s_k0[kBlock * D];
@@ -242,11 +252,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   // k_scale is read-only for the kernel's lifetime: scalar (constant-space) loads.
   const __attribute__((address_space(4))) float* ksh =
       (const __attribute__((address_space(4))) float*)(a.k_scale + bh * a.nkb);
-  // The first two K fills start before the Q codes are loaded, so that the
-  // latencies overlap (V(0) is filled by the first body).
+  // The first K and V fills start before the Q codes are loaded, so that the
+  // latencies overlap.
   if (n_ep > 0) {
     k_tile_to_lds<D>(krs, 0, s_k0, w, lane);
-    if (n_ep > 1) k_tile_to_lds<D>(krs, kBlock * D, s_k1, w, lane);
+    v_tile_to_lds<D>(vrs, 0, s_v0, w, lane);
   }
 
   v4i qreg[D / 32];
@@ -261,154 +271,101 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   v16f ro[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) ro[cb] = v16f{};
-
-  v16i sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
-  v8i pba = {}, pbb = {};  // E4M3 P of even / odd epochs
-  // The first body's deferred PV step ("epoch -1") multiplies a zero P with
-  // s_v1; zeroing s_v1 keeps garbage (NaN codes) out of that product, so it
-  // adds exactly +0 to RO.
-#pragma unroll
-  for (int i = threadIdx.x; i < D * kBlock / 16; i += kThreads) reinterpret_cast<v4i*>(s_v1)[i] = v4i{};
-  __builtin_amdgcn_s_waitcnt(0);  // the first K fills (issued above) have landed
-  __syncthreads();
-  if (w_ep > 0) qk_epoch<D>(s_k0, qreg, lane, sa0, sa1);
-  // The first epoch refills s_k0 with K(2): every wave must have read K(0) first.
-  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_waitcnt(0);  // the first fills (issued above) have landed
   __syncthreads();
 
-  // A operand of one PV step: channels 32 cb + ql, this lane's 32 keys.
-  auto pv_frag = [&](const uint8_t* vb, int cb) -> v8i {
-    const int ch = 32 * cb + ql;
-    const v4i lo = *reinterpret_cast<const v4i*>(vb + v_lds_off(ch, 2 * h));
-    const v4i hi = *reinterpret_cast<const v4i*>(vb + v_lds_off(ch, 2 * h + 1));
-    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  // p = exp2(S c - m) for 4 consecutive keys of this lane, packed to E4M3
+  // and added to the row sum in key order.
+  auto p4 = [&](const int (&x)[32], int d, float c, float m_use, float& ps) -> int {
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)x[4 * d + j], c, -m_use));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ps = (d == 0 && j == 0) ? p[0] : ps + p[j];
+    return pack4_fp8(p[0], p[1], p[2], p[3]);
   };
-  // Whole PV step of one epoch (used where nothing is left to interleave).
-  auto pv_step = [&](const uint8_t* vb, const v8i& pb) {
+  auto p4_masked = [&](const int (&x)[32], int d, float c, float m_use, int dlim, float& ps) -> int {
+    float p[4];
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-      ro[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pv_frag(vb, cb), pb, ro[cb], 0, 0, 0, 127, 0, 127);
-  };
-  // Trace checkpoint: RO after the PV step of epoch ep.
-  auto trace_ro = [&](int ep) {
-    if (TRACE && w == a.trace_wave) {
-      float* rt = a.tr_ro + ((long)ql * a.nkb + ep) * D;
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) rt[32 * cb + 8 * (r / 4) + 4 * h + r % 4] = ro[cb][r];
+    for (int j = 0; j < 4; ++j) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)x[4 * d + j], c, -m_use));
+      p[j] = (4 * d + j > dlim) ? 0.0f : e;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ps = (d == 0 && j == 0) ? p[0] : ps + p[j];
+    return pack4_fp8(p[0], p[1], p[2], p[3]);
   };
 
-  // One pipelined epoch: `cur` holds S(e), `nxt` receives S(e+1); `pbp` is
-  // P(e-1), whose PV step runs in this body, `pbn` receives P(e). The epoch's
-  // parity is a template argument so every LDS buffer is a fixed object.
-  auto body = [&](auto parity, const int e, const v16i& cur0, const v16i& cur1, v16i& nxt0, v16i& nxt1,
-                  const v8i& pbp, v8i& pbn) {
+  // One epoch. The epoch's parity is a template argument so every LDS buffer
+  // is a fixed object.
+  auto body = [&](auto parity, const int e) {
     constexpr int P = decltype(parity)::value;
-    uint8_t* k_fill = P ? s_k1 : s_k0;   // K(e+2) replaces K(e)
-    uint8_t* k_next = P ? s_k0 : s_k1;   // K(e+1)
-    uint8_t* v_prev = P ? s_v0 : s_v1;   // V(e-1)
-    uint8_t* v_fill = P ? s_v1 : s_v0;   // V(e) replaces V(e-2)
-    if (e + 2 < n_ep) k_tile_to_lds<D>(krs, (e + 2) * kBlock * D, k_fill, w, lane);
-    v_tile_to_lds<D>(vrs, e * D * kBlock, v_fill, w, lane);
-    // A wave whose last epoch was e-1 (the workgroup stages more for the
-    // other waves) runs one more body: every key of epoch e is past each of
-    // its rows' limits, so p = 0, alpha = 1 and m, l stay, and the body only
-    // completes the PV step of epoch e-1.
-    if (e < w_ep || (e == w_ep && e > 0)) {
-      // First K fragments of epoch e+1, read ahead of the row max.
-      const int key0 = qk_row_key(ql, 0), key1 = qk_row_key(ql, 1);
-      const v4i kf0 = *reinterpret_cast<const v4i*>(k_next + k_lds_off<D>(key0, h));
-      const v4i kf1 = *reinterpret_cast<const v4i*>(k_next + k_lds_off<D>(key1, h));
-      __builtin_amdgcn_sched_barrier(0);
+    uint8_t* k_cur = P ? s_k1 : s_k0;   // K(e)
+    uint8_t* v_cur = P ? s_v1 : s_v0;   // V(e)
+    uint8_t* k_fill = P ? s_k0 : s_k1;  // K(e+1) replaces K(e-1)
+    uint8_t* v_fill = P ? s_v0 : s_v1;  // V(e+1) replaces V(e-1)
+    if (e + 1 < n_ep) {
+      k_tile_to_lds<D>(krs, (e + 1) * kBlock * D, k_fill, w, lane);
+      v_tile_to_lds<D>(vrs, (e + 1) * D * kBlock, v_fill, w, lane);
+    }
+    if (e < w_ep) {
+      v16i acc0, acc1;
+      qk_epoch<D>(k_cur, qreg, lane, acc0, acc1);
       // log2-domain score per unit of the int32 accumulator
       const float c = cq * ksh[e];
       int x[32];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        x[r] = cur0[r];
-        x[16 + r] = cur1[r];
+        x[r] = acc0[r];
+        x[16 + r] = acc1[r];
       }
       const bool masked = kBlock * e + kBlock - 1 > w_lim;  // wave-uniform
       const int dlim = lim - (kBlock * e + 32 * h);          // x[t] visible iff t <= dlim
-      // Hidden scores are left in x (their p is zeroed below) and only kept
-      // out of the row max, so the unmasked path carries no select or copy.
-      int mx;
+      float ps;
+      v8i pb;
+      float alpha;
+      bool moved;
+      // Hidden scores are only kept out of the row max and have p = 0, so the
+      // unmasked path carries no select.
       if (masked) {
-        asm volatile("" ::: "memory");  // keeps the selects inside this branch
         int y[32];
 #pragma unroll
         for (int t = 0; t < 32; ++t) y[t] = (t > dlim) ? INT_MIN : x[t];
-        mx = row_max32(y);
+        const int mx = half_max(row_max32(y));
+        const float mt = (kBlock * e <= lim) ? (float)mx * c : -INFINITY;
+        const float m_new = fmaxf(m, mt);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        alpha = __builtin_amdgcn_exp2f(m - m_use);
+        moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) pb[d] = p4_masked(x, d, c, m_use, dlim, ps);
+        m = m_new;
       } else {
-        mx = row_max32(x);
+        const int mx = half_max(row_max32(x));
+        const float mt = (float)mx * c;
+        const float m_new = fmaxf(m, mt);
+        alpha = __builtin_amdgcn_exp2f(m - m_new);
+        moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) pb[d] = p4(x, d, c, m_new, ps);
+        m = m_new;
       }
-      mx = half_max(mx);
-      const float mt = (kBlock * e <= lim) ? (float)mx * c : -INFINITY;
-      const float m_new = fmaxf(m, mt);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      const bool moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;  // wave-uniform
-
-      // p = exp2(S c - m), with matrix-core steps spread through it so that
-      // each runs while this wave keeps issuing VALU work (a burst would stall
-      // the wave on each step's dependent successor). Per 32 channels, four
-      // slots: QK of epoch e+1 into each accumulator, then the PV step of
-      // epoch e-1 (RO += V(e-1)^T . P(e-1)^T, deferred one body so that it
-      // overlaps this softmax; same operands and order as an undeferred step,
-      // so RO then holds epochs < e and the rescale below applies alpha(e)
-      // before the PV step of epoch e adds into it), then VALU only. On the
-      // wave's last epoch the QK steps read a stale K buffer and go unused.
-      constexpr int kG = D / 32;
-      constexpr int kPer = 32 / (4 * kG);  // p values per slot
-      // Each operand is read from LDS right after the step that frees its
-      // registers, two or three slots ahead of its own step.
-      float p[32];
-      v4i ka = kf0, kb = kf1;
-      v8i av;
-#pragma unroll
-      for (int j = 0; j < 4 * kG; ++j) {
-        const int st = j >> 2, slot = j & 3;
-        if (slot == 0) {
-          if (st == 0) av = pv_frag(v_prev, 0);
-          nxt0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qreg[st], st ? nxt0 : v16i{}, 0, 0, 0);
-        } else if (slot == 1) {
-          if (st + 1 < kG) ka = *reinterpret_cast<const v4i*>(k_next + k_lds_off<D>(key0, 2 * (st + 1) + h));
-          nxt1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kb, qreg[st], st ? nxt1 : v16i{}, 0, 0, 0);
-        } else if (slot == 2) {
-          if (st + 1 < kG) kb = *reinterpret_cast<const v4i*>(k_next + k_lds_off<D>(key1, 2 * (st + 1) + h));
-          ro[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pbp, ro[st], 0, 0, 0, 127, 0, 127);
-        } else {
-          if (st + 1 < kG) av = pv_frag(v_prev, st + 1);
-        }
-#pragma unroll
-        for (int t = kPer * j; t < kPer * (j + 1); ++t)
-          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)x[t], c, -m_use));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (masked) {
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int t = 0; t < 32; ++t) p[t] = (t > dlim) ? 0.0f : p[t];
-      }
-      float ps = p[0];
-#pragma unroll
-      for (int t = 1; t < 32; ++t) ps += p[t];
       l = __builtin_fmaf(l, alpha, ps);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) pbn[d] = pack4_fp8(p[4 * d], p[4 * d + 1], p[4 * d + 2], p[4 * d + 3]);
-      if (e > 0) trace_ro(e - 1);
-
       // Per-tile rescale; a no-op (alpha == 1 in every lane) when no row max moved.
       if (moved) {
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) ro[cb] *= alpha;
       }
-      m = m_new;
-      if (TRACE && w == a.trace_wave && e < w_ep) {
-        // Checkpoints of this epoch: m (log2 domain), l, alpha, P8 (RO follows
-        // with the PV step in the next body).
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+        const int ch = 32 * cb + ql;
+        const v4i lo = *reinterpret_cast<const v4i*>(v_cur + v_lds_off(ch, 2 * h));
+        const v4i hi = *reinterpret_cast<const v4i*>(v_cur + v_lds_off(ch, 2 * h + 1));
+        const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        ro[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, ro[cb], 0, 0, 0, 127, 0, 127);
+      }
+      if (TRACE && w == a.trace_wave) {
+        // Checkpoints of this epoch: m (log2 domain), l, alpha, P8, RO.
         const float lt = half_sum(l);
         if (h == 0) {
           float* st = a.tr_stats + ((long)ql * (a.nkb + 1) + e) * 4;
@@ -419,7 +376,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
         }
         uint32_t* p8 = reinterpret_cast<uint32_t*>(a.tr_p8 + ((long)ql * a.nkb + e) * kBlock + 32 * h);
 #pragma unroll
-        for (int d = 0; d < 8; ++d) p8[d] = (uint32_t)pbn[d];
+        for (int d = 0; d < 8; ++d) p8[d] = (uint32_t)pb[d];
+        float* rt = a.tr_ro + ((long)ql * a.nkb + e) * D;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) rt[32 * cb + 8 * (r / 4) + 4 * h + r % 4] = ro[cb][r];
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -427,17 +389,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
   };
 
   for (int e = 0; e < n_ep; e += 2) {
-    body(std::integral_constant<int, 0>{}, e, sa0, sa1, sb0, sb1, pbb, pba);
-    if (e + 1 < n_ep) body(std::integral_constant<int, 1>{}, e + 1, sb0, sb1, sa0, sa1, pba, pbb);
-  }
-  // The PV step of the last epoch, when it is this wave's (V(e) sits in
-  // buffer e % 2; no fills are in flight any more).
-  if (w_ep > 0 && w_ep == n_ep) {
-    if ((n_ep - 1) & 1)
-      pv_step(s_v1, pbb);
-    else
-      pv_step(s_v0, pba);
-    trace_ro(n_ep - 1);
+    body(std::integral_constant<int, 0>{}, e);
+    if (e + 1 < n_ep) body(std::integral_constant<int, 1>{}, e + 1);
   }
 
   // Epilogue: the two halves of a query hold partial sums of l.
@@ -470,8 +423,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnArgs a) {
 // ------------------------------------------------------------ debug kernels
 
 // One 64x64 int32 QK tile per workgroup (2 waves = 64 queries), through the
-// same staging and qk_epoch code as the main loop's first epoch (later epochs
-// interleave the same MFMA steps, same operands, with the softmax).
+// same staging and qk_epoch code as the main loop.
 template <int D>
 __global__ __launch_bounds__(128) void qk_debug_kernel(QkDebugArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBlock * D];
