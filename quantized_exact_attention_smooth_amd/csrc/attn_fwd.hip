@@ -180,10 +180,6 @@ __device__ __forceinline__ float half_sum(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-// s_waitcnt with lgkmcnt(0) and the vector-memory and export counters left
-// at their maxima: LDS operations done, global loads and fills still in flight.
-constexpr int kWaitLgkmOnly = 0xC07F;
-
 // ------------------------------------------------------------ main kernel
 //
 // Per wave, one body per epoch e:

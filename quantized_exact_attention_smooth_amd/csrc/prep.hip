@@ -11,7 +11,8 @@
 //   quant    - one read of Q, K, V per 64-row block: block absmax, codes.
 // Every value is bit-identical to the definitions in sage_attn.h: the fp64
 // channel sum of bf16 inputs is exact (the sum of any subset is representable),
-// so the split order does not matter; divisions are IEEE fp32/fp64.
+// so the split order does not matter; every quotient is the correctly rounded
+// fp32 (or fp64) one, as an IEEE division gives.
 #include "sage_device.h"
 #include "sage_launch.h"
 
