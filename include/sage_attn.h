@@ -15,7 +15,8 @@
  *  - q is [B][H][Lq][D], k, v are [B][H][Lkv][D], out is [B][H][Lq][D]:
  *    bf16 (raw 16-bit storage), D contiguous, base address 16-byte aligned.
  *  - D is 64 or 128; B, H, Lq, Lkv >= 1; B*H*max(Lq,Lkv)*D < 2^40, and one
- *    head's K codes fit in 2 GiB: NKB*64*D < 2^31 (Lkv < 2^24 at D = 128).
+ *    head's K codes fit in 2 GiB: NKB*64*D < 2^31 (Lkv < 2^24 at D = 128);
+ *    B*H*(NQB + 2*NKB) < 2^31 (workgroups of the preparation pass).
  *  - Quantization blocks and attention epochs are SAGE_BLOCK = 64 rows/keys;
  *    NQB = ceil(Lq/64), NKB = ceil(Lkv/64).
  *  - stream is a hipStream_t (NULL = the default stream). Calls only enqueue

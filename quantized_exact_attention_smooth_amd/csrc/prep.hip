@@ -30,8 +30,9 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const uint16_t* __
   __shared__ double s_sum[kRowsPerIter][D];
   __shared__ float s_max[kRowsPerIter][D];
 
-  const int split = blockIdx.x;
-  const long bh = blockIdx.y;
+  // One-dimensional grid (its y extent is capped at 2^16): split-minor.
+  const int split = (int)(blockIdx.x % n_split);
+  const long bh = blockIdx.x / n_split;
   const int tid = threadIdx.x;
   const int cg = tid % kLanesPerRow, rg = tid / kLanesPerRow;
   const int t0 = split * kStatRows;
@@ -284,8 +285,10 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[D * kBlock];
   __shared__ float s_ch[D];  // K channel mean, or V channel scale
   __shared__ float s_rv[D];  // RN(1 / V channel scale)
-  const int job = blockIdx.x;
-  const long bh = blockIdx.y;
+  // One-dimensional grid (its y extent is capped at 2^16): job-minor.
+  const int n_jobs = a.nqb + 2 * a.nkb;
+  const int job = (int)(blockIdx.x % n_jobs);
+  const long bh = blockIdx.x / n_jobs;
   // The block's data loads are issued before the per-head channel values are
   // read, so the two memory latencies overlap.
   if (job < a.nqb) {
@@ -323,7 +326,8 @@ int prep_n_split(int Lkv) { return (Lkv + kStatRows - 1) / kStatRows; }
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   const int ns = prep_n_split(a.Lkv);
-  const dim3 g_stats(ns, BH), g_fin(BH), g_quant(a.nqb + 2 * a.nkb, BH);
+  // The host bounds both flattened grids below 2^31 workgroups.
+  const dim3 g_stats((unsigned)((long)ns * BH)), g_fin(BH), g_quant((unsigned)((long)(a.nqb + 2 * a.nkb) * BH));
   if (a.D == 128) {
     prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();

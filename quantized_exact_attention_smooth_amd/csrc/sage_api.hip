@@ -21,6 +21,10 @@ int check_dims(int B, int H, int Lq, int Lkv, int D) {
   if (elems >= 1099511627776.0) return SAGE_ERR_INVALID_ARG;  // 2^40
   const double qtiles = (double)B * H * ((Lq + sage::kQTile - 1) / sage::kQTile);
   if (qtiles >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
+  // One-dimensional preparation grids: B*H times the splits or the blocks.
+  const double nqb = (Lq + sage::kBlock - 1) / sage::kBlock, nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
+  if ((double)B * H * (nqb + 2 * nkb) >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
+  if ((double)B * H * sage::prep_n_split(Lkv) >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
   // The main loop addresses one head's K or V codes with 32-bit buffer offsets.
   const double head_codes = (double)((Lkv + sage::kBlock - 1) / sage::kBlock) * sage::kBlock * D;
   if (head_codes >= 2147483648.0) return SAGE_ERR_INVALID_ARG;
@@ -57,7 +61,7 @@ size_t prep_scratch(int B, int H, int Lkv, int D) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
-// sage_quant_prep.
+// Body of sage_quant_prep (also run by sage_attn_fwd on its workspace).
 int quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
                int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, uint8_t* v_fp8,
                float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {

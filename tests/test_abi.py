@@ -69,6 +69,9 @@ def test_size_queries_validate_shapes(lib):
     assert _ws(lib, 1, 1, 64, (1 << 24) - 64, 128)[0] == 0
     assert _ws(lib, 1, 1, 64, (1 << 24) - 63, 128)[0] == -1
     assert _ws(lib, 1, 1, 64, 1 << 25, 64)[0] == -1
+    # the preparation pass launches B*H*(NQB + 2*NKB) workgroups in one dimension
+    assert _ws(lib, 1 << 14, 1 << 15, 1, 1, 64)[0] == 0
+    assert _ws(lib, 1 << 15, 1 << 15, 1, 1, 64)[0] == -1
     assert lib.sage_workspace_bytes(1, 1, 64, 64, 64, None) == -1
 
 

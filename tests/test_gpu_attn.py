@@ -17,7 +17,7 @@ import torch
 import oracle
 import seeded_inputs as si
 import quantized_exact_attention_smooth_amd as sage
-from _parity import assert_out_close, oracle_preps, oracle_rows, say
+from _parity import assert_out_close, assert_prep_equal, oracle_preps, oracle_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -184,3 +184,29 @@ def test_oracle_accuracy_holds_for_gpu_output(gpu_device):
         a = oracle.bf16_to_f32(out[0, h]).astype(np.float64).ravel()
         cos = a @ ref.ravel() / math.sqrt((a @ a) * (ref.ravel() @ ref.ravel()))
         assert cos >= 0.995, (h, cos)
+
+
+def test_more_heads_than_a_grid_dimension_holds(gpu_device):
+    # B*H = 72000 heads (> 2^16, the largest y extent of a launch grid): 17
+    # seeded heads repeated, a period chosen so that a head index that wrapped
+    # at 2^16 would pick different data. The last heads are checked against
+    # the oracle, prepared operands bit for bit and outputs to the tolerance.
+    B, H, L, D, period = 2, 36000, 64, 64, 17
+    q0, k0, v0 = si.make_qkv(1, period, L, L, D, "normal", 2.0, seed=31)
+    idx = torch.arange(B * H) % period
+    dev = gpu_device
+    qg, kg, vg = (t[0].to(dev)[idx].reshape(B, H, L, D).contiguous() for t in (q0, k0, v0))
+    say(f"{B}x{H} heads, L={L} D={D} causal")
+    p = sage.quant_prep(qg, kg, vg)
+    out = si.bf16_bits(sage.attn_fwd_prepped(p, True, 0.125))
+    torch.cuda.synchronize()
+    g = {n: p[n][:, -2:].cpu().numpy() for n in ("q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "v_scale")}
+    vv = p["v_fp8"][:, -2:].cpu().numpy()
+    g["v8"] = vv.transpose(0, 1, 2, 4, 3).reshape(B, 2, -1, D)
+    del p, qg, kg, vg
+    for b in range(B):
+        for j, h in enumerate((H - 2, H - 1)):
+            src = (b * H + h) % period
+            o = oracle.prep_head(si.bf16_bits(q0[0, src]), si.bf16_bits(k0[0, src]), si.bf16_bits(v0[0, src]))
+            assert_prep_equal(g, o, b, j)
+            assert_out_close(out[b, h], oracle.attn_rows(o, True, 0.125), f"head ({b},{h})")
