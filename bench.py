@@ -136,8 +136,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards over (b, h) heads with no exchange, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU (asked for --gpus {args.gpus}); the path shards over (b, h) "
+              "heads with no exchange between GPUs, and only the one-GPU kernel is run", file=sys.stderr)
         return 3
 
     import torch
