@@ -17,7 +17,7 @@ import torch
 import oracle
 import seeded_inputs as si
 import quantized_exact_attention_smooth_amd as sage
-from _parity import assert_out_close, assert_prep_equal, oracle_preps, oracle_rows, say
+from _parity import assert_out_close, assert_prep_equal, gpu_prep_numpy, oracle_preps, oracle_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -210,3 +210,32 @@ def test_more_heads_than_a_grid_dimension_holds(gpu_device):
             o = oracle.prep_head(si.bf16_bits(q0[0, src]), si.bf16_bits(k0[0, src]), si.bf16_bits(v0[0, src]))
             assert_prep_equal(g, o, b, j)
             assert_out_close(out[b, h], oracle.attn_rows(o, True, 0.125), f"head ({b},{h})")
+
+
+def _random_shapes(n=24, seed=20261202):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        out.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 700)),
+                    int(rng.integers(1, 700)), D, bool(rng.integers(0, 2)),
+                    str(rng.choice(["normal", "student_t_outlier"])), float(rng.choice([0.0, 2.0, 4.0])), i))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Lq,Lkv,D,causal,dist,sigma,seed", _random_shapes())
+def test_seeded_random_shapes(B, H, Lq, Lkv, D, causal, dist, sigma, seed, gpu_device):
+    # Shapes, masks and value distributions drawn from a fixed seed: every
+    # head against the oracle, prepared operands bit for bit and outputs to
+    # the tolerance.
+    say(f"random shape {seed}: {(B, H, Lq, Lkv, D, causal, dist, sigma)}")
+    q, k, v = si.make_qkv(B, H, Lq, Lkv, D, dist, sigma, seed=1000 + seed)
+    sc = 1 / math.sqrt(D)
+    qg, kg, vg = q.to(gpu_device), k.to(gpu_device), v.to(gpu_device)
+    p = sage.quant_prep(qg, kg, vg)
+    out = si.bf16_bits(sage.attn_fwd_prepped(p, causal, sc))
+    torch.cuda.synchronize()
+    g = gpu_prep_numpy(p)
+    for (b, h), o in oracle_preps(q, k, v, [(b, h) for b in range(B) for h in range(H)]).items():
+        assert_prep_equal(g, o, b, h)
+        assert_out_close(out[b, h], oracle_rows(o, causal, sc, 0, Lq), f"head {(b, h)}")
