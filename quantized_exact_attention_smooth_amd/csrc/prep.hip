@@ -87,19 +87,22 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const uint16_t* __
 }
 
 // Per head: mean = fp32(sum / Lkv) and sv = absmax / 448 from the split
-// partials. The kThreads / D thread groups of a channel each take every
-// G-th split with four loads in flight, then combine through LDS; the fp64
-// partial sums are exact, so the order does not matter.
+// partials. A workgroup takes kFinChannels channels of one head; its
+// kThreads / kFinChannels thread groups each take every G-th split with four
+// loads in flight, then combine through LDS. The fp64 partial sums are exact,
+// so the order does not matter.
+constexpr int kFinChannels = 32;
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_finalize_kernel(const double* __restrict__ psum,
                                                                  const float* __restrict__ pmax, int n_split,
                                                                  int Lkv, float* __restrict__ k_mean,
                                                                  float* __restrict__ v_scale) {
-  constexpr int G = kThreads / D;
-  __shared__ double s_sum[G][D];
-  __shared__ float s_max[G][D];
-  const long bh = blockIdx.x;
-  const int c = threadIdx.x % D, g = threadIdx.x / D;
+  constexpr int G = kThreads / kFinChannels;
+  __shared__ double s_sum[G][kFinChannels];
+  __shared__ float s_max[G][kFinChannels];
+  const long bh = blockIdx.x / (D / kFinChannels);
+  const int cl = threadIdx.x % kFinChannels, g = threadIdx.x / kFinChannels;
+  const int c = (int)(blockIdx.x % (D / kFinChannels)) * kFinChannels + cl;
   const double* ps = psum + bh * n_split * (long)D + c;
   const float* pm = pmax + bh * n_split * (long)D + c;
   double a[4] = {0.0, 0.0, 0.0, 0.0};
@@ -116,16 +119,16 @@ __global__ __launch_bounds__(kThreads) void prep_finalize_kernel(const double* _
     a[0] += ps[(long)s * D];
     m[0] = fmaxf(m[0], pm[(long)s * D]);
   }
-  s_sum[g][c] = (a[0] + a[1]) + (a[2] + a[3]);
-  s_max[g][c] = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+  s_sum[g][cl] = (a[0] + a[1]) + (a[2] + a[3]);
+  s_max[g][cl] = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
   __syncthreads();
   if (g == 0) {
     double t = 0.0;
     float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      t += s_sum[i][c];
-      mx = fmaxf(mx, s_max[i][c]);
+      t += s_sum[i][cl];
+      mx = fmaxf(mx, s_max[i][cl]);
     }
     k_mean[bh * D + c] = (float)(t / (double)Lkv);
     v_scale[bh * D + c] = mx / 448.0f;
@@ -327,7 +330,8 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
   const int BH = a.B * a.H;
   const int ns = prep_n_split(a.Lkv);
   // The host bounds both flattened grids below 2^31 workgroups.
-  const dim3 g_stats((unsigned)((long)ns * BH)), g_fin(BH), g_quant((unsigned)((long)(a.nqb + 2 * a.nkb) * BH));
+  const dim3 g_stats((unsigned)((long)ns * BH)), g_fin((unsigned)((long)BH * (a.D / kFinChannels))),
+      g_quant((unsigned)((long)(a.nqb + 2 * a.nkb) * BH));
   if (a.D == 128) {
     prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();

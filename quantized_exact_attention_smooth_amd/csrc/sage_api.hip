@@ -21,10 +21,12 @@ int check_dims(int B, int H, int Lq, int Lkv, int D) {
   if (elems >= 1099511627776.0) return SAGE_ERR_INVALID_ARG;  // 2^40
   const double qtiles = (double)B * H * ((Lq + sage::kQTile - 1) / sage::kQTile);
   if (qtiles >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
-  // One-dimensional preparation grids: B*H times the splits or the blocks.
+  // One-dimensional preparation grids: B*H times the splits, the blocks or the
+  // 32-channel groups.
   const double nqb = (Lq + sage::kBlock - 1) / sage::kBlock, nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
   if ((double)B * H * (nqb + 2 * nkb) >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
   if ((double)B * H * sage::prep_n_split(Lkv) >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
+  if ((double)B * H * (D / 32) >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
   // The main loop addresses one head's K or V codes with 32-bit buffer offsets.
   const double head_codes = (double)((Lkv + sage::kBlock - 1) / sage::kBlock) * sage::kBlock * D;
   if (head_codes >= 2147483648.0) return SAGE_ERR_INVALID_ARG;
