@@ -9,6 +9,9 @@
 //   finalize - per head: mean = fp32(sum / Lkv), sv = absmax / 448 (the
 //              splits spread over the workgroup);
 //   quant    - one read of Q, K, V per 64-row block: block absmax, codes.
+// With few splits per head (short keys) the finalize launch is skipped: each
+// K or V workgroup of the quantization pass reduces the splits of its head
+// itself, and the head's first K and V workgroups write the means and scales.
 // Every value is bit-identical to the definitions in sage_attn.h: the fp64
 // channel sum of bf16 inputs is exact (the sum of any subset is representable),
 // so the split order does not matter; every quotient is the correctly rounded
@@ -280,6 +283,27 @@ __device__ void quant_v_block(const VBlockLoad<D>& ld, int L, int blk, const flo
   }
 }
 
+// Most statistics splits per head for which the quantization workgroups reduce
+// the splits themselves instead of a finalize launch (each K or V workgroup
+// then reads n_split * D partials of its head).
+constexpr int kFuseMaxSplits = 4;
+
+// Channel c's mean and V scale of head bh from the split partials, with the
+// finalize pass's arithmetic (the fp64 partial sums are exact, so the order
+// does not matter).
+__device__ __forceinline__ float head_mean(const PrepArgs& a, long bh, int c) {
+  const double* ps = a.psum + bh * (long)a.n_split * a.D + c;
+  double t = 0.0;
+  for (int s = 0; s < a.n_split; ++s) t += ps[(long)s * a.D];
+  return (float)(t / (double)a.Lkv);
+}
+__device__ __forceinline__ float head_vscale(const PrepArgs& a, long bh, int c) {
+  const float* pm = a.pmax + bh * (long)a.n_split * a.D + c;
+  float m = 0.0f;
+  for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, pm[(long)s * a.D]);
+  return m / 448.0f;
+}
+
 // One workgroup per (tensor, 64-row block): job in [0, nqb) codes a Q block,
 // [nqb, nqb + nkb) a K block, [nqb + nkb, nqb + 2 nkb) a V block.
 template <int D>
@@ -303,7 +327,15 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
     const int blk = job - a.nqb;
     Int8BlockLoad<D> ld;
     ld.load(a.k + bh * (long)a.Lkv * D, a.Lkv, blk);
-    if (threadIdx.x < D) s_ch[threadIdx.x] = a.k_mean[bh * D + threadIdx.x];
+    if (threadIdx.x < D) {
+      if (a.fuse_finalize) {
+        const float mu = head_mean(a, bh, threadIdx.x);
+        s_ch[threadIdx.x] = mu;
+        if (blk == 0) a.k_mean[bh * D + threadIdx.x] = mu;
+      } else {
+        s_ch[threadIdx.x] = a.k_mean[bh * D + threadIdx.x];
+      }
+    }
     __syncthreads();
     quant_int8_block<D>(ld, a.Lkv, blk, s_ch, a.k_i8 + bh * (long)a.nkb * kBlock * D,
                         a.k_scale + bh * a.nkb + blk, s_red);
@@ -313,7 +345,13 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
     ld.load(a.v + bh * (long)a.Lkv * D, a.Lkv, blk);
     bool tiny = false;
     if (threadIdx.x < D) {
-      const float s = a.v_scale[bh * D + threadIdx.x];
+      float s;
+      if (a.fuse_finalize) {
+        s = head_vscale(a, bh, threadIdx.x);
+        if (blk == 0) a.v_scale[bh * D + threadIdx.x] = s;
+      } else {
+        s = a.v_scale[bh * D + threadIdx.x];
+      }
       s_ch[threadIdx.x] = s;
       tiny = s != 0.0f && !(s >= kFastDivMinScale);
       s_rv[threadIdx.x] = tiny || s == 0.0f ? 0.0f : 1.0f / s;
@@ -326,9 +364,12 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
 
 int prep_n_split(int Lkv) { return (Lkv + kStatRows - 1) / kStatRows; }
 
-hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
+hipError_t launch_prep(const PrepArgs& args, hipStream_t stream) {
+  PrepArgs a = args;
   const int BH = a.B * a.H;
   const int ns = prep_n_split(a.Lkv);
+  a.n_split = ns;
+  a.fuse_finalize = ns <= kFuseMaxSplits;
   // The host bounds both flattened grids below 2^31 workgroups.
   const dim3 g_stats((unsigned)((long)ns * BH)), g_fin((unsigned)((long)BH * (a.D / kFinChannels))),
       g_quant((unsigned)((long)(a.nqb + 2 * a.nkb) * BH));
@@ -336,15 +377,19 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
     prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    prep_finalize_kernel<128><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!a.fuse_finalize) {
+      prep_finalize_kernel<128><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     prep_quant_kernel<128><<<g_quant, kThreads, 0, stream>>>(a);
   } else {
     prep_stats_kernel<64><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    prep_finalize_kernel<64><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!a.fuse_finalize) {
+      prep_finalize_kernel<64><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     prep_quant_kernel<64><<<g_quant, kThreads, 0, stream>>>(a);
   }
   return hipGetLastError();

@@ -24,6 +24,8 @@ struct PrepArgs {
   float* v_scale;
   double* psum;  // [B*H][n_split][D] fp64 channel partial sums of K
   float* pmax;   // [B*H][n_split][D] channel absmax partials of V
+  int n_split;   // statistics splits per head
+  int fuse_finalize;  // 1: the quantization workgroups reduce the splits themselves
 };
 
 struct AttnArgs {

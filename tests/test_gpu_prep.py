@@ -36,8 +36,12 @@ def test_prep_bit_exact_on_workload(idx, gpu_device):
             assert_prep_equal(g, o, b, h)
 
 
+# Lkv = 1024 and 1025 sit on either side of the largest key count whose
+# statistics splits the quantization workgroups reduce themselves (four splits
+# of 256 keys); longer keys take the separate finalize launch.
 SHAPES = [(1, 1, 1, 1, 64), (1, 2, 63, 65, 128), (2, 1, 64, 64, 64), (1, 1, 65, 1, 128), (1, 3, 1000, 129, 64),
-          (1, 1, 129, 1000, 128), (1, 1, 255, 257, 128), (2, 2, 300, 511, 64)]
+          (1, 1, 129, 1000, 128), (1, 1, 255, 257, 128), (2, 2, 300, 511, 64), (1, 2, 100, 1024, 128),
+          (1, 2, 100, 1025, 64)]
 
 
 @pytest.mark.parametrize("B,H,Lq,Lkv,D", SHAPES)
