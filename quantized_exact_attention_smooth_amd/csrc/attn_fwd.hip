@@ -88,19 +88,28 @@ struct VStage {
 
 // ------------------------------------------------------------ QK, codecs
 
+// LDS byte offsets of this lane's A-operand reads in qk_epoch: step s reads
+// key qk_row_key(row, 0), chunk 2s + h at koff[s], and the key 16 rows
+// further down at koff[s] + 16 D (the swizzle does not depend on key bit 4).
+template <int D>
+__device__ __forceinline__ void qk_offsets(int lane, int (&koff)[D / 32]) {
+  const int row = lane & 31, h = lane >> 5;
+  const int key0 = qk_row_key(row, 0);
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) koff[s] = k_lds_off<D>(key0, 2 * s + h);
+}
+
 // Exact int32 scores of one 64-key epoch for the 32 queries of a wave.
 // lane = (h, q): acc_m[r] = S[q][32h + 16m + r] for m = 0, 1.
 template <int D>
-__device__ __forceinline__ void qk_epoch(const uint8_t* lk, const v4i* qreg, int lane, v16i& acc0,
-                                         v16i& acc1) {
-  const int row = lane & 31, h = lane >> 5;
-  const int key0 = qk_row_key(row, 0), key1 = qk_row_key(row, 1);
+__device__ __forceinline__ void qk_epoch(const uint8_t* lk, const v4i* qreg, const int (&koff)[D / 32],
+                                         v16i& acc0, v16i& acc1) {
   acc0 = v16i{};
   acc1 = v16i{};
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
-    const v4i a0 = *reinterpret_cast<const v4i*>(lk + k_lds_off<D>(key0, 2 * s + h));
-    const v4i a1 = *reinterpret_cast<const v4i*>(lk + k_lds_off<D>(key1, 2 * s + h));
+    const v4i a0 = *reinterpret_cast<const v4i*>(lk + koff[s]);
+    const v4i a1 = *reinterpret_cast<const v4i*>(lk + koff[s] + 16 * D);
     acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, qreg[s], acc0, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, qreg[s], acc1, 0, 0, 0);
   }
@@ -263,6 +272,13 @@ void attn_fwd_kernel(AttnArgs a) {
   const float sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
   const float cq = sq * a.scale_log2;
 
+  // The QK read offsets are computed once; the empty asm keeps the compiler
+  // from rebuilding them from their parts in every epoch (four VALU adds).
+  int koff[D / 32];
+  qk_offsets<D>(lane, koff);
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) asm volatile("" : "+v"(koff[s]));
+
   float m = -INFINITY, l = 0.0f;
   v16f ro[D / 32];
 #pragma unroll
@@ -306,7 +322,7 @@ void attn_fwd_kernel(AttnArgs a) {
     }
     if (e < w_ep) {
       v16i acc0, acc1;
-      qk_epoch<D>(k_cur, qreg, lane, acc0, acc1);
+      qk_epoch<D>(k_cur, qreg, koff, acc0, acc1);
       // log2-domain score per unit of the int32 accumulator
       const float c = cq * ksh[e];
       int x[32];
@@ -438,7 +454,9 @@ __global__ __launch_bounds__(128) void qk_debug_kernel(QkDebugArgs a) {
   ks.store(s_k);
   __syncthreads();
   v16i acc0, acc1;
-  qk_epoch<D>(s_k, qreg, lane, acc0, acc1);
+  int koff[D / 32];
+  qk_offsets<D>(lane, koff);
+  qk_epoch<D>(s_k, qreg, koff, acc0, acc1);
   int32_t* o = a.acc_out + (long)t * kBlock * kBlock + (32 * w + ql) * kBlock + 32 * h;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
