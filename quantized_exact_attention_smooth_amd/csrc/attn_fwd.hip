@@ -218,6 +218,9 @@ void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k1[kBlock * D];
   __shared__ __attribute__((aligned(16))) uint8_t s_v0[D * kBlock];
   __shared__ __attribute__((aligned(16))) uint8_t s_v1[D * kBlock];
+  // The head's V channel scales, read at the start so that the epilogue does
+  // not wait for a global load.
+  __shared__ __attribute__((aligned(16))) float s_sv[D];
 
   const int BH = a.B * a.H;
   const int tile = TRACE ? a.trace_tile : a.n_qtiles - 1 - (int)(blockIdx.x / BH);
@@ -271,6 +274,7 @@ void attn_fwd_kernel(AttnArgs a) {
     qreg[s] = (qrow < a.Lq) ? *reinterpret_cast<const v4i*>(qh + (long)qrow * D + 32 * s + 16 * h) : v4i{};
   const float sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
   const float cq = sq * a.scale_log2;
+  if (threadIdx.x < D) s_sv[threadIdx.x] = a.v_scale[bh * D + threadIdx.x];
 
   // The QK read offsets are computed once; the empty asm keeps the compiler
   // from rebuilding them from their parts in every epoch (four VALU adds).
@@ -417,13 +421,12 @@ void attn_fwd_kernel(AttnArgs a) {
   }
   if (qrow < a.Lq) {
     uint16_t* orow = a.out + (bh * a.Lq + qrow) * (long)D;
-    const float* svh = a.v_scale + bh * D;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c0 = 32 * cb + 8 * g + 4 * h;
-        const float4 sv = *reinterpret_cast<const float4*>(svh + c0);
+        const float4 sv = *reinterpret_cast<const float4*>(s_sv + c0);
         const uint32_t w0 = pack2_bf16(ro[cb][4 * g + 0] * rcp * sv.x, ro[cb][4 * g + 1] * rcp * sv.y);
         const uint32_t w1 = pack2_bf16(ro[cb][4 * g + 2] * rcp * sv.z, ro[cb][4 * g + 3] * rcp * sv.w);
         *reinterpret_cast<uint2*>(orow + c0) = make_uint2(w0, w1);
