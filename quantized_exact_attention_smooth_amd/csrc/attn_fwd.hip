@@ -46,46 +46,6 @@
 
 namespace sage {
 
-// ---------------------------------------------------------------- staging
-
-// Copy one K tile (64 x D int8, row-major) into LDS with the read swizzle.
-template <int D, int NT>
-struct KStage {
-  static constexpr int kChunks = kBlock * D / 16 / NT;
-  v4i r[kChunks];
-  __device__ __forceinline__ void load(const int8_t* __restrict__ src) {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j)
-      r[j] = *reinterpret_cast<const v4i*>(src + 16 * (threadIdx.x + NT * j));
-  }
-  __device__ __forceinline__ void store(uint8_t* lds) const {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int g = threadIdx.x + NT * j;
-      *reinterpret_cast<v4i*>(lds + k_lds_off<D>(g / (D / 16), g % (D / 16))) = r[j];
-    }
-  }
-};
-
-// Copy one V tile (D x 64 e4m3, keys contiguous) into LDS with the swizzle.
-template <int D, int NT>
-struct VStage {
-  static constexpr int kChunks = D * kBlock / 16 / NT;
-  v4i r[kChunks];
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ src) {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j)
-      r[j] = *reinterpret_cast<const v4i*>(src + 16 * (threadIdx.x + NT * j));
-  }
-  __device__ __forceinline__ void store(uint8_t* lds) const {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int g = threadIdx.x + NT * j;
-      *reinterpret_cast<v4i*>(lds + v_lds_off(g / 4, g % 4)) = r[j];
-    }
-  }
-};
-
 // ------------------------------------------------------------ QK, codecs
 
 // LDS byte offsets of this lane's A-operand reads in qk_epoch: step s reads
@@ -438,23 +398,30 @@ void attn_fwd_kernel(AttnArgs a) {
 // ------------------------------------------------------------ debug kernels
 
 // One 64x64 int32 QK tile per workgroup (2 waves = 64 queries), through the
-// same staging and qk_epoch code as the main loop.
+// main loop's own staging (direct buffer-to-LDS copies into the swizzled
+// layout) and qk_epoch code.
 template <int D>
 __global__ __launch_bounds__(128) void qk_debug_kernel(QkDebugArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kBlock * D];
   const int t = blockIdx.x;
   const long bh = (long)a.tiles[t][0] * a.H + a.tiles[t][1];
   const int qb = a.tiles[t][2], kb = a.tiles[t][3];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, ql = lane & 31;
+  const int lane = threadIdx.x & 63, h = lane >> 5, ql = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int qrow = qb * kBlock + 32 * w + ql;
   v4i qreg[D / 32];
   const int8_t* qh = a.q_i8 + bh * (long)a.nqb * kBlock * D;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s)
     qreg[s] = *reinterpret_cast<const v4i*>(qh + (long)qrow * D + 32 * s + 16 * h);
-  KStage<D, 128> ks;
-  ks.load(a.k_i8 + (bh * a.nkb + kb) * (long)kBlock * D);
-  ks.store(s_k);
+  // The two waves copy the four quarters of the tile that the main loop's
+  // four waves copy (the host bounds a head's codes below 2^31 bytes).
+  const int head_bytes = a.nkb * kBlock * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k_i8 + bh * (long)head_bytes), (short)0, head_bytes, kRawBufferFlags);
+  k_tile_to_lds<D>(krs, kb * kBlock * D, s_k, w, lane);
+  k_tile_to_lds<D>(krs, kb * kBlock * D, s_k, w + 2, lane);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   v16i acc0, acc1;
   int koff[D / 32];
