@@ -379,19 +379,33 @@ void attn_fwd_kernel(AttnArgs a) {
     st[2] = 0.0f;
     st[3] = 0.0f;
   }
-  if (qrow < a.Lq) {
-    uint16_t* orow = a.out + (bh * a.Lq + qrow) * (long)D;
+  // A wave's 32 output rows are consecutive in memory. The bf16 values go
+  // through LDS (one of the four K/V buffers per wave; every wave has passed
+  // the last epoch's barrier, so none is read any more) and leave as whole
+  // 16-byte chunks of consecutive rows: scattered 8-byte stores of the
+  // register layout cost more than the arithmetic of the epilogue.
+  uint8_t* stage = w == 0 ? s_k0 : w == 1 ? s_k1 : w == 2 ? s_v0 : s_v1;  // 32 rows x 2D bytes
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) {
+  for (int cb = 0; cb < D / 32; ++cb) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c0 = 32 * cb + 8 * g + 4 * h;
-        const float4 sv = *reinterpret_cast<const float4*>(s_sv + c0);
-        const uint32_t w0 = pack2_bf16(ro[cb][4 * g + 0] * rcp * sv.x, ro[cb][4 * g + 1] * rcp * sv.y);
-        const uint32_t w1 = pack2_bf16(ro[cb][4 * g + 2] * rcp * sv.z, ro[cb][4 * g + 3] * rcp * sv.w);
-        *reinterpret_cast<uint2*>(orow + c0) = make_uint2(w0, w1);
-      }
+    for (int g = 0; g < 4; ++g) {
+      const int c0 = 32 * cb + 8 * g + 4 * h;
+      const float4 sv = *reinterpret_cast<const float4*>(s_sv + c0);
+      const uint32_t w0 = pack2_bf16(ro[cb][4 * g + 0] * rcp * sv.x, ro[cb][4 * g + 1] * rcp * sv.y);
+      const uint32_t w1 = pack2_bf16(ro[cb][4 * g + 2] * rcp * sv.z, ro[cb][4 * g + 3] * rcp * sv.w);
+      *reinterpret_cast<uint2*>(stage + out_lds_off<D>(ql, 4 * cb + g) + 8 * h) = make_uint2(w0, w1);
     }
+  }
+  // A wave's LDS accesses complete in order; this keeps the compiler from
+  // moving the reads below above the writes.
+  asm volatile("" ::: "memory");
+  constexpr int kChunksPerRow = D / 8;  // 16-byte chunks of one bf16 output row
+  uint16_t* obase = a.out + (bh * a.Lq + wrow0) * (long)D;
+#pragma unroll
+  for (int i = 0; i < 32 * kChunksPerRow / 64; ++i) {
+    const int gi = lane + 64 * i, row = gi / kChunksPerRow, chunk = gi % kChunksPerRow;
+    const uint4 val = *reinterpret_cast<const uint4*>(stage + out_lds_off<D>(row, chunk));
+    if (wrow0 + row < a.Lq) *reinterpret_cast<uint4*>(obase + (long)row * D + 8 * chunk) = val;
   }
 }
 

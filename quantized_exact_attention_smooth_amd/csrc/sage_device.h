@@ -64,6 +64,17 @@ __device__ __forceinline__ int v_lds_off(int c, int chunk) {
   return c * 64 + ((chunk ^ (((c >> 1) ^ (c >> 2)) & 3)) << 4);
 }
 
+// Byte offset of 16-byte chunk `chunk` of row `row` in a wave's LDS staging
+// area for its 32 bf16 output rows (2D bytes each). The chunk index is XORed
+// with row bits so that the register-layout writes (one 8-byte half chunk per
+// lane, 32 rows at once) fall in at most two lanes per bank and the row-order
+// reads (16 lanes per 256 bytes) in one.
+template <int D>
+__device__ __forceinline__ int out_lds_off(int row, int chunk) {
+  const int f = D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return row * 2 * D + ((chunk ^ f) << 4);
+}
+
 // A-operand row -> key mapping of the QK matrix-core step. The 32x32 int32
 // result gives lane (h = lane/32, q = lane%32), register r the row
 // 8*(r/4) + 4*h + (r%4). Loading key 32*h + 16*m + 4*(row/8) + (row%4) for
