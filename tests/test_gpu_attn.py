@@ -239,3 +239,30 @@ def test_seeded_random_shapes(B, H, Lq, Lkv, D, causal, dist, sigma, seed, gpu_d
     for (b, h), o in oracle_preps(q, k, v, [(b, h) for b in range(B) for h in range(H)]).items():
         assert_prep_equal(g, o, b, h)
         assert_out_close(out[b, h], oracle_rows(o, causal, sc, 0, Lq), f"head {(b, h)}")
+
+
+def _times_pow2(t: torch.Tensor, e: int) -> torch.Tensor:
+    """2^e times a bf16 tensor (exact for these values: all stay normal)."""
+    return (t.float() * 2.0 ** e).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_power_of_two_scalings_act_exactly(causal, gpu_device):
+    """The oracle's metamorphic pins, on the GPU path bit for bit: V times 2^5
+    scales the output by exactly 2^5; K times 2^-7 with sm_scale times 2^7,
+    and Q times 2^3 with sm_scale times 2^-3, leave it unchanged (every scale
+    the kernels form is a product or quotient that a power of two passes
+    through exactly: means, block and channel scales, reciprocals, the
+    folded log2-domain factor)."""
+    B, H, L, D = 1, 2, 333, 128
+    say(f"attn parity: power-of-two scalings, causal={causal}")
+    q, k, v = si.make_qkv(B, H, L, L, D, "normal", 2.0, seed=77)
+    sc = 1 / math.sqrt(D)
+    out = _gpu_out(q, k, v, causal, sc, gpu_device, end_to_end=True)
+    out_f = oracle.bf16_to_f32(out).astype(np.float64)
+    got_v = _gpu_out(q, k, _times_pow2(v, 5), causal, sc, gpu_device, end_to_end=True)
+    np.testing.assert_array_equal(oracle.bf16_to_f32(got_v).astype(np.float64), out_f * 2.0 ** 5)
+    got_k = _gpu_out(q, _times_pow2(k, -7), v, causal, sc * 2.0 ** 7, gpu_device, end_to_end=True)
+    np.testing.assert_array_equal(got_k, out)
+    got_q = _gpu_out(_times_pow2(q, 3), k, v, causal, sc * 2.0 ** -3, gpu_device, end_to_end=True)
+    np.testing.assert_array_equal(got_q, out)

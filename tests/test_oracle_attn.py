@@ -235,3 +235,44 @@ def test_smoothing_ablation_large_k_offset():
     assert min(with_s) >= 0.995
     for a, b in zip(with_s, without):
         assert (1 - b) > 1.5 * (1 - a)
+
+
+def _scaled_bits(bits: np.ndarray, e: int) -> np.ndarray:
+    """bf16 bits of 2^e times the bf16 values (exact: no value leaves the
+    normal range in these tests)."""
+    x = oracle.bf16_to_f32(bits).astype(np.float64) * 2.0 ** e
+    assert np.all((x == 0) | ((np.abs(x) >= 2.0 ** -126) & (np.abs(x) < 2.0 ** 127)))
+    return _bits(x)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("e", [-9, 6])
+def test_power_of_two_scalings_act_exactly(causal, e):
+    """Metamorphic pins of where each scale enters, bit for bit: every scale
+    of the contract is a quotient or product that a power of two passes
+    through exactly. V times 2^e: the channel scales gain 2^e, the E4M3 codes
+    stay, and the output is 2^e times the original. K times 2^e with sm_scale
+    times 2^-e: the K means and block scales gain 2^e, the codes stay, and the
+    scores and output are unchanged (likewise for Q). A scale applied twice
+    or dropped, or sm_scale applied to the wrong factor, fails one of these."""
+    L, D = 200, 64
+    q, k, v = si.make_qkv(1, 1, L, L, D, "normal", 2.0, seed=31 + e)
+    qb, kb, vb = (si.bf16_bits(t)[0, 0] for t in (q, k, v))
+    sc = 1 / math.sqrt(D)
+    base = oracle.prep_head(qb, kb, vb)
+    out = oracle.attn_rows(base, causal, sc)
+
+    pv = oracle.prep_head(qb, kb, _scaled_bits(vb, e))
+    np.testing.assert_array_equal(pv["v8"], base["v8"])
+    np.testing.assert_array_equal(pv["v_scale"], base["v_scale"] * np.float32(2.0 ** e))
+    np.testing.assert_array_equal(oracle.attn_rows(pv, causal, sc), _scaled_bits(out, e))
+
+    pk = oracle.prep_head(qb, _scaled_bits(kb, e), vb)
+    np.testing.assert_array_equal(pk["k8"], base["k8"])
+    np.testing.assert_array_equal(pk["k_scale"], base["k_scale"] * np.float32(2.0 ** e))
+    np.testing.assert_array_equal(pk["k_mean"], base["k_mean"] * np.float32(2.0 ** e))
+    np.testing.assert_array_equal(oracle.attn_rows(pk, causal, sc * 2.0 ** -e), out)
+
+    pq = oracle.prep_head(_scaled_bits(qb, e), kb, vb)
+    np.testing.assert_array_equal(pq["q8"], base["q8"])
+    np.testing.assert_array_equal(oracle.attn_rows(pq, causal, sc * 2.0 ** -e), out)
