@@ -291,16 +291,26 @@ constexpr int kFuseMaxSplits = 4;
 // Channel c's mean and V scale of head bh from the split partials, with the
 // finalize pass's arithmetic (the fp64 partial sums are exact, so the order
 // does not matter).
+// All of a channel's partials are loaded before any is added, so their
+// latencies overlap (and overlap the block's own loads, issued earlier).
 __device__ __forceinline__ float head_mean(const PrepArgs& a, long bh, int c) {
   const double* ps = a.psum + bh * (long)a.n_split * a.D + c;
+  double x[kFuseMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kFuseMaxSplits; ++s) x[s] = s < a.n_split ? ps[(long)s * a.D] : 0.0;
   double t = 0.0;
-  for (int s = 0; s < a.n_split; ++s) t += ps[(long)s * a.D];
+#pragma unroll
+  for (int s = 0; s < kFuseMaxSplits; ++s) t += x[s];
   return (float)(t / (double)a.Lkv);
 }
 __device__ __forceinline__ float head_vscale(const PrepArgs& a, long bh, int c) {
   const float* pm = a.pmax + bh * (long)a.n_split * a.D + c;
+  float x[kFuseMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kFuseMaxSplits; ++s) x[s] = s < a.n_split ? pm[(long)s * a.D] : 0.0f;
   float m = 0.0f;
-  for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, pm[(long)s * a.D]);
+#pragma unroll
+  for (int s = 0; s < kFuseMaxSplits; ++s) m = fmaxf(m, x[s]);
   return m / 448.0f;
 }
 
