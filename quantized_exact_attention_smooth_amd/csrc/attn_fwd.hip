@@ -309,19 +309,23 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int t = 0; t < 32; ++t) y[t] = (t > dlim) ? INT_MIN : x[t];
         const int mx = half_max(row_max32(y));
         const float mt = (kBlock * e <= lim) ? (float)mx * c : -INFINITY;
-        const float m_new = fmaxf(m, mt);
+        // mt > m is the only way the running max changes (neither is NaN), so
+        // one compare gives both the new max and the lanes that moved.
+        const bool up = mt > m;
+        const float m_new = up ? mt : m;
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         alpha = __builtin_amdgcn_exp2f(m - m_use);
-        moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
+        moved = __builtin_amdgcn_ballot_w64(up) != 0;
 #pragma unroll
         for (int d = 0; d < 8; ++d) pb[d] = p4_masked(x, d, c, m_use, dlim, ps);
         m = m_new;
       } else {
         const int mx = half_max(row_max32(x));
         const float mt = (float)mx * c;
-        const float m_new = fmaxf(m, mt);
+        const bool up = mt > m;
+        const float m_new = up ? mt : m;
         alpha = __builtin_amdgcn_exp2f(m - m_new);
-        moved = __builtin_amdgcn_ballot_w64(m_new != m) != 0;
+        moved = __builtin_amdgcn_ballot_w64(up) != 0;
 #pragma unroll
         for (int d = 0; d < 8; ++d) pb[d] = p4(x, d, c, m_new, ps);
         m = m_new;
