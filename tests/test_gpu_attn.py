@@ -266,3 +266,41 @@ def test_power_of_two_scalings_act_exactly(causal, gpu_device):
     np.testing.assert_array_equal(got_k, out)
     got_q = _gpu_out(_times_pow2(q, 3), k, v, causal, sc * 2.0 ** -3, gpu_device, end_to_end=True)
     np.testing.assert_array_equal(got_q, out)
+
+
+def test_concurrent_calls_on_two_streams_match_sequential(gpu_device):
+    """Calls keep no state between them: two host threads, each on its own
+    stream (default priority), run different shapes at the same time, and
+    every output equals the one from a sequential run bit for bit."""
+    import threading
+    say("attn parity: concurrent calls on two streams")
+    cases = [((1, 4, 777, 777, 128), True, 11), ((2, 2, 300, 1025, 64), False, 12)]
+    inputs = [tuple(t.to(gpu_device) for t in si.make_qkv(*shape, "normal", 2.0, seed))
+              for shape, _, seed in cases]
+    seq = []
+    for (shape, causal, _), (q, k, v) in zip(cases, inputs):
+        seq.append(si.bf16_bits(sage.attn_fwd(q, k, v, causal, 1 / math.sqrt(shape[4]))))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=gpu_device) for _ in cases]
+    results = [None] * len(cases)
+    errors = []
+
+    def run(i):
+        try:
+            (shape, causal, _), (q, k, v) = cases[i], inputs[i]
+            with torch.cuda.stream(streams[i]):
+                outs = [sage.attn_fwd(q, k, v, causal, 1 / math.sqrt(shape[4])) for _ in range(3)]
+            streams[i].synchronize()
+            results[i] = [si.bf16_bits(o) for o in outs]
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(len(cases)):
+        for got in results[i]:
+            np.testing.assert_array_equal(got, seq[i])
