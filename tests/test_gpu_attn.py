@@ -304,3 +304,36 @@ def test_concurrent_calls_on_two_streams_match_sequential(gpu_device):
     for i in range(len(cases)):
         for got in results[i]:
             np.testing.assert_array_equal(got, seq[i])
+
+
+def test_graph_replays_match_eager_runs(gpu_device):
+    """sage_attn_fwd allocates nothing and issues no memset or host
+    synchronisation, so a captured HIP graph of it replays correctly: four
+    replays, with eager work and synchronisation between them and new input
+    values copied in before some, each equal bit for bit to an eager call on
+    the same inputs."""
+    say("attn parity: HIP graph replays")
+    B, H, L, D, causal = 1, 3, 500, 128, True
+    sc = 1 / math.sqrt(D)
+    q, k, v = (t.to(gpu_device) for t in si.make_qkv(B, H, L, L, D, "normal", 2.0, seed=21))
+    ws = torch.empty(sage.workspace_bytes(B, H, L, L, D), dtype=torch.uint8, device=gpu_device)
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream(device=gpu_device)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sage.attn_fwd(q, k, v, causal, sc, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sage.attn_fwd(q, k, v, causal, sc, out=out, workspace=ws)
+    for r in range(4):
+        if r % 2 == 1:  # new input values in the captured buffers
+            nq, nk, nv = si.make_qkv(B, H, L, L, D, "normal", 2.0, seed=100 + r)
+            q.copy_(nq.to(gpu_device)), k.copy_(nk.to(gpu_device)), v.copy_(nv.to(gpu_device))
+        expect = si.bf16_bits(sage.attn_fwd(q, k, v, causal, sc))
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(si.bf16_bits(out), expect)
