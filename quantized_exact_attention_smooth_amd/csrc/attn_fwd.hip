@@ -35,7 +35,9 @@
 //    i.e. alpha == 1 in every lane), then the matrix core reduces the epoch's
 //    64 keys in fp32 (inner level) and adds the result into RO, its C
 //    operand (outer level).
-//  * epilogue: r = 1/l (IEEE divide), out = bf16(RO * r * sv[c]) for rows < Lq.
+//  * epilogue: r = 1/l (IEEE divide), out = bf16(RO * r * sv[c]) for rows < Lq,
+//    with sv read into LDS at the start; a wave's 32 rows are consecutive in
+//    memory, so they pass through LDS and leave as whole 16-byte chunks.
 //  * instantiations: TRACE records one wave's per-epoch state (debug).
 #include <limits.h>
 
