@@ -337,3 +337,28 @@ def test_graph_replays_match_eager_runs(gpu_device):
         graph.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(si.bf16_bits(out), expect)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_largest_key_count_zero_q_constant_v_is_exact(causal, gpu_device):
+    """The largest key count the library admits at D = 128: one head's K and
+    V codes fill 2^31 - 8192 bytes, the limit of the main loop's 32-bit buffer
+    offsets (262,143 epochs, 65,536 statistics splits). With Q = 0 every score
+    is 0, so p = 1 for each visible key, l counts them exactly (< 2^24), every
+    V code is +-448 and every partial sum of RO is an exactly representable
+    multiple of 448: the output is bf16(v_c) in every row, whatever K holds."""
+    B, H, Lq, D = 1, 1, 256, 128
+    Lkv = (1 << 24) - 64
+    say(f"zero Q, constant V at the largest key count: Lq={Lq} Lkv={Lkv} causal={causal}")
+    gen = torch.Generator(device=gpu_device)
+    gen.manual_seed(2024 + causal)
+    k = torch.randn((B, H, Lkv, D), generator=gen, device=gpu_device, dtype=torch.float32).to(torch.bfloat16)
+    vc = torch.from_numpy(np.random.default_rng(9).normal(0, 2, D).astype(np.float32)).to(torch.bfloat16)
+    v = vc.to(gpu_device).reshape(1, 1, 1, D).expand(B, H, Lkv, D).contiguous()
+    q = torch.zeros((B, H, Lq, D), dtype=torch.bfloat16, device=gpu_device)
+    out = sage.attn_fwd(q, k, v, causal, 1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    got = si.bf16_bits(out)[0, 0]
+    del k, v, out
+    torch.cuda.empty_cache()
+    np.testing.assert_array_equal(got, np.broadcast_to(si.bf16_bits(vc), (Lq, D)))
