@@ -339,16 +339,21 @@ def test_graph_replays_match_eager_runs(gpu_device):
         np.testing.assert_array_equal(si.bf16_bits(out), expect)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_largest_key_count_zero_q_constant_v_is_exact(causal, gpu_device):
-    """The largest key count the library admits at D = 128: one head's K and
-    V codes fill 2^31 - 8192 bytes, the limit of the main loop's 32-bit buffer
-    offsets (262,143 epochs, 65,536 statistics splits). With Q = 0 every score
-    is 0, so p = 1 for each visible key, l counts them exactly (< 2^24), every
-    V code is +-448 and every partial sum of RO is an exactly representable
-    multiple of 448: the output is bf16(v_c) in every row, whatever K holds."""
-    B, H, Lq, D = 1, 1, 256, 128
-    Lkv = (1 << 24) - 64
+def test_largest_key_count_zero_q_constant_v_is_exact(D, causal, gpu_device):
+    """The largest key count the library admits: one head's K and V codes
+    fill 2^31 - 64 D bytes, the limit of the main loop's 32-bit buffer
+    offsets (2^24 - 64 keys at D = 128, 2^25 - 64 at D = 64; 262,143 or
+    524,287 epochs and 65,536 or 131,072 statistics splits). With Q = 0 every score
+    is 0, so p = 1 for each visible key and every V code is +-448. RO's
+    partial sums, multiples of 64 * 448 = 7 * 2^12 over at most 2^19 epochs,
+    are exact in fp32, and so is each lane half's share of the key count
+    (< 2^24); their total is within 2^-25 of the count. The output is
+    therefore bf16(v_c) in every row, whatever K holds (the fp32 errors are
+    far below half a bf16 ulp)."""
+    B, H, Lq = 1, 1, 256
+    Lkv = (1 << 31) // D - 64
     say(f"zero Q, constant V at the largest key count: Lq={Lq} Lkv={Lkv} causal={causal}")
     gen = torch.Generator(device=gpu_device)
     gen.manual_seed(2024 + causal)
