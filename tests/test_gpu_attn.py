@@ -367,3 +367,26 @@ def test_largest_key_count_zero_q_constant_v_is_exact(D, causal, gpu_device):
     del k, v, out
     torch.cuda.empty_cache()
     np.testing.assert_array_equal(got, np.broadcast_to(si.bf16_bits(vc), (Lq, D)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_largest_query_count_zero_q_constant_v_is_exact(causal, gpu_device):
+    """2^24 - 64 query rows against 200 keys (D = 128; 131,072 main-loop
+    workgroups, 4 GiB of output). Zero Q and constant V give bf16(v_c) in
+    every row that sees a key; causal (bottom-right) rows above the last
+    Lkv see none and output 0. Compared on the GPU."""
+    B, H, D, Lkv = 1, 1, 128, 200
+    Lq = (1 << 24) - 64
+    say(f"zero Q, constant V at the largest query count: Lq={Lq} Lkv={Lkv} causal={causal}")
+    k = si.make_qkv(B, H, 1, Lkv, D, "normal", 2.0, seed=5)[1].to(gpu_device)
+    vc = torch.from_numpy(np.random.default_rng(10).normal(0, 2, D).astype(np.float32)).to(torch.bfloat16)
+    v = vc.to(gpu_device).reshape(1, 1, 1, D).expand(B, H, Lkv, D).contiguous()
+    q = torch.zeros((B, H, Lq, D), dtype=torch.bfloat16, device=gpu_device)
+    out = sage.attn_fwd(q, k, v, causal, 1 / math.sqrt(D))
+    vcd = vc.to(gpu_device).view(torch.int16)
+    got = out.view(torch.int16)[0, 0]
+    first = Lq - Lkv if causal else 0  # rows before this one see no key
+    assert bool((got[first:] == vcd).all())
+    assert bool((got[:first] == 0).all())
+    del q, out, got
+    torch.cuda.empty_cache()
