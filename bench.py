@@ -104,6 +104,57 @@ def cpu_baseline(w) -> dict:
             "fp64_reference": {"rows": n_ref, "s": dt_ref}}
 
 
+# The one timing the pages print for this method: the fast attention kernel of
+# the Phase 2B fixed aligned prototype (Experiment Log), one head of
+# Q128 x KV192 x D128, batched p50 and single-launch p50 on an SM121 GPU.
+# Other hardware: context for the same shape, not a baseline of the metric.
+PAGES_FIXTURE_P50_MS = {"batched": 0.014426, "single_launch": 0.016288}
+
+
+def fixture_latency(lib, dev, stream) -> dict:
+    """Main-kernel latency at the pages' fixture shape (workload 0): p50 of 20
+    batches of 20 launches and of 2000 single launches, HIP events on the
+    launch stream."""
+    import torch
+    import seeded_inputs as si
+    import quantized_exact_attention_smooth_amd as sage
+
+    w = si.WORKLOADS[0]
+    q, k, v = (t.to(dev) for t in si.workload_qkv(w))
+    p = sage.quant_prep(q, k, v)
+    out = torch.empty_like(q)
+    sp = stream.cuda_stream
+
+    def launch():
+        sage._lib.check("sage_attn_fwd_prepped", lib.sage_attn_fwd_prepped(
+            p["q_i8"].data_ptr(), p["q_scale"].data_ptr(), p["k_i8"].data_ptr(), p["k_scale"].data_ptr(),
+            p["v_fp8"].data_ptr(), p["v_scale"].data_ptr(), out.data_ptr(), w.B, w.H, w.Lq, w.Lkv, w.D,
+            int(w.causal), w.sm_scale, sp))
+
+    for _ in range(200):
+        launch()
+    torch.cuda.synchronize()
+    batches = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            launch()
+        e1.record(stream)
+        e1.synchronize()
+        batches.append(e0.elapsed_time(e1) / 20)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2000)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    singles = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return {"workload": w.name, "main_batched_p50_ms": sorted(batches)[len(batches) // 2],
+            "main_single_p50_ms": singles[len(singles) // 2],
+            "pages_sm121_p50_ms": PAGES_FIXTURE_P50_MS}
+
+
 def copy_calibration(nbytes: int, steps: int) -> int:
     """A plain device-to-device copy of known size: its FETCH_SIZE and
     WRITE_SIZE counter readings scale the main kernel's readings to bytes."""
@@ -277,6 +328,8 @@ def main() -> int:
         "prep_frac_hbm": prep_bytes / (prep_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "e2e_ms": e2e_avg, "e2e_tops": ops / (e2e_avg * 1e-3) / 1e12,
     }
+    if args.workload is None and not args.shape:
+        rec["fixture_q128_kv192"] = fixture_latency(L, dev, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
