@@ -66,7 +66,14 @@ int sage_workspace_bytes(int B, int H, int Lq, int Lkv, int D, size_t* bytes);
  * Preparation pass (Experiment Log, "Phase 0 Import And Verification":
  * Q/K preparation, K smoothing, INT8 quantization, FP8 V).
  * Inputs q, k, v as above. Outputs (device, caller-owned):
- *   k_mean  fp32 [B][H][D]        mean[c] = fp32(fp64 sum_t K[t][c] / Lkv)
+ *   k_mean  fp32 [B][H][D]        mean[c] = fp32(fp64 sum_t K[t][c] / Lkv);
+ *                                  the fp64 sum runs in an unspecified order.
+ *                                  It is exact, so the mean is order-free,
+ *                                  when the channel's nonzero |K| lie in
+ *                                  [2^e_min, 2^(e_max+1)), e_max - e_min <=
+ *                                  45 - ceil(log2 Lkv) (bf16 has 8
+ *                                  significant bits); otherwise its last
+ *                                  bits may depend on the order
  *   k_i8    int8 [B][H][NKB*64][D] codes of Ks = fp32(K) - mean, per 64-row
  *                                  block: s = absmax/127, code =
  *                                  clamp(rint_even(Ks / s), -127, 127)

@@ -27,23 +27,37 @@ _lock = threading.Lock()
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile liboracle.so with gcc (plain C11, -O2, no FMA contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+# ORACLE_SANITIZE=1 selects a build with AddressSanitizer and
+# UndefinedBehaviorSanitizer (host code only; the process must preload the
+# sanitizer runtimes, e.g. LD_PRELOAD="$(gcc -print-file-name=libasan.so)
+# $(gcc -print-file-name=libubsan.so)" ASAN_OPTIONS=detect_leaks=0).
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def _sanitize() -> bool:
+    return os.environ.get("ORACLE_SANITIZE", "") == "1"
+
+
+def build(force: bool = False, sanitize: bool = None) -> str:
+    """Compile liboracle.so with gcc (plain C11, -O2, no FMA contraction);
+    with sanitize (default: ORACLE_SANITIZE=1) the instrumented variant."""
+    sanitize = _sanitize() if sanitize is None else sanitize
+    lib = _SAN_LIB if sanitize else _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-               "-Wall", "-o", tmp, _SRC, "-lm"]
+               "-Wall", *(_SAN_FLAGS if sanitize else []), "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = ctypes.CDLL(_LIB)
+            lib = ctypes.CDLL(build())
             P = ctypes.c_void_p
             I = ctypes.c_int
             L = ctypes.c_long

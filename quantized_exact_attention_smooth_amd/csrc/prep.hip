@@ -12,10 +12,14 @@
 // With few splits per head (short keys) the finalize launch is skipped: each
 // K or V workgroup of the quantization pass reduces the splits of its head
 // itself, and the head's first K and V workgroups write the means and scales.
-// Every value is bit-identical to the definitions in sage_attn.h: the fp64
-// channel sum of bf16 inputs is exact (the sum of any subset is representable),
-// so the split order does not matter; every quotient is the correctly rounded
-// fp32 (or fp64) one, as an IEEE division gives.
+// Every quotient is the correctly rounded fp32 (or fp64) one, as an IEEE
+// division gives. The K channel sums are fp64 sums over 256-row splits, then
+// over the splits: bf16 values carry 8 significant bits, so when a channel's
+// nonzero magnitudes lie in [2^e_min, 2^(e_max + 1)) with
+// e_max - e_min <= 45 - ceil(log2 Lkv), every partial sum is a multiple of
+// 2^(e_min - 7) of magnitude below 2^53 such units: exact, so the split order
+// cannot change a bit of the mean. Outside that range (values spread over more binades) the
+// last bits of the sum, and rarely of the fp32 mean, may depend on the order.
 #include "sage_device.h"
 #include "sage_launch.h"
 
@@ -92,8 +96,8 @@ __global__ __launch_bounds__(kThreads) void prep_stats_kernel(const uint16_t* __
 // Per head: mean = fp32(sum / Lkv) and sv = absmax / 448 from the split
 // partials. A workgroup takes kFinChannels channels of one head; its
 // kThreads / kFinChannels thread groups each take every G-th split with four
-// loads in flight, then combine through LDS. The fp64 partial sums are exact,
-// so the order does not matter.
+// loads in flight, then combine through LDS (the order matters only when the
+// channel sum is not exact; see the file header).
 constexpr int kFinChannels = 32;
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_finalize_kernel(const double* __restrict__ psum,
@@ -289,8 +293,8 @@ __device__ void quant_v_block(const VBlockLoad<D>& ld, int L, int blk, const flo
 constexpr int kFuseMaxSplits = 4;
 
 // Channel c's mean and V scale of head bh from the split partials, with the
-// finalize pass's arithmetic (the fp64 partial sums are exact, so the order
-// does not matter).
+// finalize pass's arithmetic (exact sums, so the same bits as the finalize
+// pass, under the condition in the file header).
 // All of a channel's partials are loaded before any is added, so their
 // latencies overlap (and overlap the block's own loads, issued earlier).
 __device__ __forceinline__ float head_mean(const PrepArgs& a, long bh, int c) {

@@ -276,3 +276,63 @@ def test_power_of_two_scalings_act_exactly(causal, e):
     pq = oracle.prep_head(_scaled_bits(qb, e), kb, vb)
     np.testing.assert_array_equal(pq["q8"], base["q8"])
     np.testing.assert_array_equal(oracle.attn_rows(pq, causal, sc * 2.0 ** -e), out)
+
+
+# ---------------------------------------------------------------------------
+# Reading R9: the denominator l sums the fp32 probabilities p before their
+# FP8 rounding ("d" and "FP8 probability" are separate checkpoints in the
+# Experiment Log's Phase 2B prototype). The two tests below fail if l summed
+# the decoded FP8 probabilities instead.
+
+def _bf16(x):
+    import torch
+    return torch.tensor(np.float32(x)).to(torch.bfloat16).view(torch.int16).item() & 0xFFFF
+
+
+def test_denominator_of_two_keys_sums_fp32_probabilities():
+    """One query, two keys, hand-computed. Q row = 127 e_0 gives s_q = 1 and
+    code 127; K rows +-127 e_0 have channel mean 0, s_k = 1 and codes +-127,
+    so the scores are z = +-(16129 * sm_scale) rounded to fp32. With sm_scale
+    chosen so that p_2 = exp(z_2 - z_1) is near 0.3: l = 1 + p_2 in fp32,
+    while the FP8 probability of key 2 is 0.3125 (E4M3 spacing 2^-5 there),
+    so a denominator of decoded FP8 values would be 1.3125."""
+    D = 64
+    q = np.zeros((1, D), np.float32)
+    q[0, 0] = 127.0
+    k = np.zeros((2, D), np.float32)
+    k[0, 0], k[1, 0] = 127.0, -127.0
+    v = np.ones((2, D), np.float32)  # constant V: V8 = 448 and sv = RN(1/448)
+    p = oracle.prep_head(oracle.bf16_round(q), oracle.bf16_round(k), oracle.bf16_round(v))
+    assert p["q_scale"][0] == 1 and p["k_scale"][0] == 1 and p["q8"][0, 0] == 127 and p["k8"][1, 0] == -127
+    sm = np.float32(math.log(1 / 0.3) / 32258.0)
+    z1 = np.float32(np.float32(16129.0) * sm)  # (acc * (sq * sk)) * sm with sq * sk = 1
+    p2 = np.float32(math.exp(-2.0 * float(z1)))
+    l_hand = np.float32(np.float32(1.0) + p2)
+    assert abs(p2 - 0.3) < 1e-6 and oracle.e4m3_decode(oracle.e4m3_encode([p2]))[0] == 0.3125
+    t = oracle.attn_row_trace(p, False, float(sm), 0)
+    assert t["stats"][0, 1] == l_hand and t["stats"][1, 1] == l_hand
+    assert list(t["p8"][0, :2]) == [0x38, int(oracle.e4m3_encode([p2])[0])]
+    r = np.float32(np.float32(1.0) / l_hand)
+    assert t["stats"][1, 0] == r
+    # RO = 448 * 1 + 448 * 0.3125 = 588 exactly; out = bf16((RO * r) * sv)
+    sv = np.float32(np.float32(1.0) / np.float32(448.0))
+    want = _bf16(np.float32(np.float32(np.float32(588.0) * r) * sv))
+    assert t["out"][0] == want and want != _bf16(1.0)
+
+
+def test_constant_v_output_reflects_fp32_denominator():
+    """V constant per channel: every V code is +-448, so out / v_c is
+    sum dec(P8) / sum p up to fp32 rounding. With the fp32 denominator this
+    ratio differs from 1 by the FP8 rounding of the weights and a sizeable
+    share of outputs leave bf16(v_c) (measured 22-38 % of the elements on
+    these shapes); with a denominator of decoded FP8 values every output
+    would be exactly bf16(v_c)."""
+    for L, D, causal in [(192, 128, False), (300, 64, True)]:
+        q, k, _ = _f64_head(L, L, D, seed=8, sigma=2.0)
+        vc = oracle.bf16_to_f32(oracle.bf16_round(np.random.default_rng(6).uniform(0.5, 2, D)
+                                                  * np.sign(np.arange(D) - 60.5)))
+        v = np.tile(vc, (L, 1))
+        p = oracle.prep_head(oracle.bf16_round(q), oracle.bf16_round(k), oracle.bf16_round(v))
+        out = oracle.attn_rows(p, causal, 1 / math.sqrt(D))
+        share = float(np.mean(out != np.tile(oracle.bf16_round(vc), (L, 1))))
+        assert share >= 0.15, (L, D, share)

@@ -10,7 +10,9 @@ whose K blocks reach absmax 860). There the oracle's output matches fp64
 attention on its own dequantized operands to cosine >= 0.9999 on every
 block, so the loss is the 64-row INT8 block contract on heavy-tailed data,
 not the epoch loop; that workload asserts the dequantized match and records
-its measured level with a floor of 0.9.
+its measured level with a floor of 0.915 (the measured minimum 0.9183 less a
+small margin). It misses the 0.995 bar; the benchmark line and the README
+say so.
 """
 import math
 
@@ -65,6 +67,6 @@ def test_workload_oracle_subset_accuracy(idx):
     print(f"{w.name}: min cosine {min(cos):.5f} over {len(work)} row chunks")
     if outlier:
         assert min(r[1] for r in res) >= 0.9999
-        assert min(cos) >= 0.9
+        assert min(cos) >= 0.915
     else:
         assert min(cos) >= 0.995
