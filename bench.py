@@ -41,7 +41,7 @@ PEAK_TOPS = 5000.0       # MI355X dense INT8 / FP8 matrix-core peak
 HBM_PEAK_GBS = 8000.0
 
 
-MAIN_KERNEL_SOURCES = ("attn_fwd.hip", "sage_device.h", "sage_launch.h")
+MAIN_KERNEL_SOURCES = ("attn_fwd.hip", "attn_split.hip", "attn_common.h", "sage_device.h", "sage_launch.h")
 
 
 def _code_text(src: str) -> str:
@@ -181,6 +181,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=None, help="index into seeded_inputs.WORKLOADS")
     ap.add_argument("--shape", type=str, default=None,
                     help="B,H,Lq,Lkv,D,causal: a custom N(0,1) workload (K offset sigma 2) instead of a named one")
+    ap.add_argument("--kernel", choices=("auto", "fused", "split"), default="auto",
+                    help="main-loop design timed in the main scope (sage_attn_fwd uses auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration only: time a plain device copy of this many bytes and exit")
@@ -232,10 +234,13 @@ def main() -> int:
             k8.data_ptr(), kscale.data_ptr(), kmean.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
             scratch.data_ptr(), n.value, sp))
 
+    kernel = {"auto": _lib.SAGE_KERNEL_AUTO, "fused": _lib.SAGE_KERNEL_FUSED, "split": _lib.SAGE_KERNEL_SPLIT}[
+        args.kernel]
+
     def main_loop():
-        _lib.check("sage_attn_fwd_prepped", L.sage_attn_fwd_prepped(
+        _lib.check("sage_attn_fwd_prepped_kernel", L.sage_attn_fwd_prepped_kernel(
             q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), kscale.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
-            out.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale, sp))
+            out.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale, kernel, sp))
 
     # end-to-end: sage_attn_fwd into a preallocated workspace
     nws = ctypes.c_size_t(0)
@@ -317,7 +322,7 @@ def main() -> int:
         "steps": K, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8+fp8_e4m3", "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "Lq": Lq, "Lkv": Lkv, "D": D, "causal": w.causal,
-                   "k_offset_sigma": w.k_offset_sigma, "dist": w.dist},
+                   "k_offset_sigma": w.k_offset_sigma, "dist": w.dist, "main_kernel": args.kernel},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_TOPS, "traffic": _traffic(w.name)},
         "main_ms": main_avg, "main_tops": achieved,

@@ -111,6 +111,34 @@ int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t
                           int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, void* stream);
 
 /*
+ * Main-loop kernel designs. Every design computes the same values bit for
+ * bit (the same per-epoch arithmetic in the same order); they differ in how
+ * the work is laid out on the waves of a workgroup.
+ *   SAGE_KERNEL_FUSED  each wave owns 32 query rows end to end: their Q
+ *                      codes, scores, running max and sum, and RO.
+ *   SAGE_KERNEL_SPLIT  wave-specialised ownership (Experiment Log, "Phase 1
+ *                      State-Ownership Decision": paired QK/softmax and
+ *                      PV/output owners; "Phase 2A": the role clocks
+ *                      overlap): softmax waves hold the Q codes, scores, m
+ *                      and l; PV waves hold RO; the E4M3 P block and alpha
+ *                      of each epoch pass between them through LDS.
+ *   SAGE_KERNEL_AUTO   the design measured faster for the shape: SPLIT when
+ *                      B*H*ceil(Lq/128) < 256 (fewer 128-row tiles than
+ *                      compute units), FUSED otherwise. sage_attn_fwd and
+ *                      sage_attn_fwd_prepped use it.
+ */
+enum sage_kernel { SAGE_KERNEL_AUTO = 0, SAGE_KERNEL_FUSED = 1, SAGE_KERNEL_SPLIT = 2 };
+
+/*
+ * sage_attn_fwd_prepped with an explicit main-loop design (enum
+ * sage_kernel); any other value returns SAGE_ERR_INVALID_ARG.
+ */
+int sage_attn_fwd_prepped_kernel(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                                 const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
+                                 int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, int kernel,
+                                 void* stream);
+
+/*
  * The whole path: sage_quant_prep into the workspace (its parts laid out as
  * sage_workspace_bytes describes), then sage_attn_fwd_prepped on them, both
  * on stream. workspace: device memory of at least sage_workspace_bytes,
@@ -134,24 +162,28 @@ int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, in
 /*
  * Debug: per-epoch checkpoints of 32 query rows (Experiment Log, "Phase 2B
  * Fixed Aligned Numerical Prototype": the QK, m, d, FP8 probability,
- * rescale, PV, FP32 RO and reciprocal checkpoints). Runs the main loop's own
- * kernel on the one 128-row tile of head (b, h) that holds rows row0 ..
- * row0 + 31 (row0 a multiple of 32, < Lq); the wave owning those rows
- * writes, for row t = row0 + i and every epoch e it computes (e below the
- * wave's epoch count; the caller pre-fills the buffers to recognise the rest):
+ * rescale, PV, FP32 RO and reciprocal checkpoints). Runs the main loop of
+ * design `kernel` (enum sage_kernel) on the one 128-row tile of head (b, h)
+ * that holds rows row0 .. row0 + 31 (row0 a multiple of 32, < Lq); the waves
+ * owning those rows write, for row t = row0 + i and every epoch e they
+ * compute (e below the rows' epoch count; the caller pre-fills the buffers
+ * to recognise the rest):
  *   stats [32][NKB+1][4] fp32: [i][e] = m (log2 domain: max of z * log2(e)),
  *         l, alpha (of this epoch), 0; [i][NKB] = 1/l, l at the end;
  *   p8    [32][NKB][64] uint8: the epoch's E4M3 P bytes, key 64e + j;
+ *   pv    [32][NKB][D]  fp32: the epoch's own PV partial, sum over its 64
+ *         keys of dec(P8) dec(V8) (the main loop adds it into RO inside
+ *         the matrix-core step; the trace build runs that step once more
+ *         into a zeroed accumulator to record it);
  *   ro    [32][NKB][D]  fp32: RO after the epoch (RO * alpha + PV).
- * PV itself is not a separate value on this hardware: the matrix core adds
- * it into RO. out (bf16 [B][H][Lq][D]) receives that tile's rows as the
- * main loop would write them. Arguments otherwise as sage_attn_fwd_prepped;
- * stats 16-byte aligned, p8 and ro 4-byte aligned.
+ * out (bf16 [B][H][Lq][D]) receives that tile's rows as the main loop would
+ * write them. Arguments otherwise as sage_attn_fwd_prepped; stats 16-byte
+ * aligned, p8, pv and ro 4-byte aligned.
  */
 int sage_debug_epoch_trace(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                            const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
-                           int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, int b, int h,
-                           int row0, float* stats, uint8_t* p8, float* ro, void* stream);
+                           int B, int H, int Lq, int Lkv, int D, int causal, float sm_scale, int kernel, int b,
+                           int h, int row0, float* stats, uint8_t* p8, float* pv, float* ro, void* stream);
 
 /*
  * Debug: run the device conversions the main loop uses on n fp32 values x

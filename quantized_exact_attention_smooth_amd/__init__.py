@@ -12,10 +12,12 @@ import math
 
 import torch
 
-from ._lib import (LIB_PATH, SAGE_BLOCK, SageError, check, lib, status_str)  # noqa: F401
+from ._lib import (LIB_PATH, SAGE_BLOCK, SAGE_KERNEL_AUTO, SAGE_KERNEL_FUSED, SAGE_KERNEL_SPLIT,  # noqa: F401
+                   SageError, check, lib, status_str)
 
 __all__ = ["workspace_bytes", "prep_scratch_bytes", "quant_prep", "attn_fwd_prepped", "attn_fwd",
-           "debug_qk_int32", "debug_codecs", "debug_epoch_trace", "SageError", "status_str", "LIB_PATH"]
+           "debug_qk_int32", "debug_codecs", "debug_epoch_trace", "SageError", "status_str", "LIB_PATH",
+           "SAGE_KERNEL_AUTO", "SAGE_KERNEL_FUSED", "SAGE_KERNEL_SPLIT"]
 
 
 def _stream(stream=None) -> int:
@@ -80,18 +82,19 @@ def quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, stream=None) -
 
 
 def attn_fwd_prepped(prep: dict, causal: bool, sm_scale: float = None, out: torch.Tensor = None,
-                     stream=None) -> torch.Tensor:
-    """sage_attn_fwd_prepped on the dict quant_prep returns."""
+                     stream=None, kernel: int = SAGE_KERNEL_AUTO) -> torch.Tensor:
+    """sage_attn_fwd_prepped_kernel on the dict quant_prep returns (kernel:
+    SAGE_KERNEL_AUTO, _FUSED or _SPLIT)."""
     B, H, Lq, Lkv, D = prep["shape"]
     if out is None:
         out = torch.empty((B, H, Lq, D), dtype=torch.bfloat16, device=prep["q_i8"].device)
-    st = lib().sage_attn_fwd_prepped(
+    st = lib().sage_attn_fwd_prepped_kernel(
         _dev(prep["q_i8"], torch.int8, "q_i8"), _dev(prep["q_scale"], torch.float32, "q_scale"),
         _dev(prep["k_i8"], torch.int8, "k_i8"), _dev(prep["k_scale"], torch.float32, "k_scale"),
         _dev(prep["v_fp8"], torch.uint8, "v_fp8"), _dev(prep["v_scale"], torch.float32, "v_scale"),
         _dev(out, torch.bfloat16, "out"), B, H, Lq, Lkv, D, int(bool(causal)),
-        float(sm_scale) if sm_scale else 0.0, _stream(stream))
-    check("sage_attn_fwd_prepped", st)
+        float(sm_scale) if sm_scale else 0.0, int(kernel), _stream(stream))
+    check("sage_attn_fwd_prepped_kernel", st)
     return out
 
 
@@ -116,15 +119,17 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, sm
 
 
 def debug_epoch_trace(prep: dict, b: int, h: int, row0: int, causal: bool, sm_scale: float = None,
-                      stream=None) -> dict:
+                      stream=None, kernel: int = SAGE_KERNEL_AUTO) -> dict:
     """sage_debug_epoch_trace: per-epoch checkpoints of rows row0 .. row0+31 of
     head (b, h). Returns stats [32, NKB+1, 4] (NaN where not written), p8
-    [32, NKB, 64] uint8 (0xFF where not written), ro [32, NKB, D] and out."""
+    [32, NKB, 64] uint8 (0xFF where not written), pv and ro [32, NKB, D] and
+    out."""
     B, H, Lq, Lkv, D = prep["shape"]
     nkb = -(-Lkv // SAGE_BLOCK)
     dev = prep["q_i8"].device
     stats = torch.full((32, nkb + 1, 4), float("nan"), dtype=torch.float32, device=dev)
     p8 = torch.full((32, nkb, SAGE_BLOCK), 0xFF, dtype=torch.uint8, device=dev)
+    pv = torch.full((32, nkb, D), float("nan"), dtype=torch.float32, device=dev)
     ro = torch.full((32, nkb, D), float("nan"), dtype=torch.float32, device=dev)
     out = torch.zeros((B, H, Lq, D), dtype=torch.bfloat16, device=dev)
     st = lib().sage_debug_epoch_trace(
@@ -132,10 +137,10 @@ def debug_epoch_trace(prep: dict, b: int, h: int, row0: int, causal: bool, sm_sc
         _dev(prep["k_i8"], torch.int8, "k_i8"), _dev(prep["k_scale"], torch.float32, "k_scale"),
         _dev(prep["v_fp8"], torch.uint8, "v_fp8"), _dev(prep["v_scale"], torch.float32, "v_scale"),
         _dev(out, torch.bfloat16, "out"), B, H, Lq, Lkv, D, int(bool(causal)),
-        float(sm_scale) if sm_scale else 0.0, int(b), int(h), int(row0), stats.data_ptr(), p8.data_ptr(),
-        ro.data_ptr(), _stream(stream))
+        float(sm_scale) if sm_scale else 0.0, int(kernel), int(b), int(h), int(row0), stats.data_ptr(),
+        p8.data_ptr(), pv.data_ptr(), ro.data_ptr(), _stream(stream))
     check("sage_debug_epoch_trace", st)
-    return dict(stats=stats, p8=p8, ro=ro, out=out)
+    return dict(stats=stats, p8=p8, pv=pv, ro=ro, out=out)
 
 
 def debug_qk_int32(prep: dict, tiles, stream=None) -> torch.Tensor:

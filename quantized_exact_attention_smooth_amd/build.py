@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsage_attn.so")
-SOURCES = ["prep.hip", "attn_fwd.hip", "sage_api.hip"]
+SOURCES = ["prep.hip", "attn_fwd.hip", "attn_split.hip", "sage_api.hip"]
 
 # -packed-fp32-ops off: no packed fp32 VALU instructions are generated.
 # -amdgpu-mfma-vgpr-form: matrix-core results land in VGPRs, which the

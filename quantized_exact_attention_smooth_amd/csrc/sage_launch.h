@@ -45,6 +45,7 @@ struct AttnArgs {
   float* tr_stats;
   uint8_t* tr_p8;
   float* tr_ro;
+  float* tr_pv;
 };
 
 constexpr int kMaxDebugTiles = 64;
@@ -56,10 +57,16 @@ struct QkDebugArgs {
   int tiles[kMaxDebugTiles][4];
 };
 
+// Main-loop kernel designs (the values of SAGE_KERNEL_* in sage_attn.h).
+constexpr int kKernelFused = 1;  // every wave runs QK, softmax and PV for its rows
+constexpr int kKernelSplit = 2;  // softmax waves and PV waves own separate state
+
 int prep_n_split(int Lkv);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
-hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream);
-hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream);
+hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream);
+hipError_t launch_attn_fused(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream);
+hipError_t launch_attn_split(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream);
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream);
 hipError_t launch_codecs_debug(const float* x, int n, uint8_t* p8, uint16_t* bf16, hipStream_t stream);
 

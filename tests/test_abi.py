@@ -30,7 +30,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("sage_quant_prep", "sage_attn_fwd", "sage_attn_fwd_prepped", "sage_workspace_bytes",
+    for n in ("sage_quant_prep", "sage_attn_fwd", "sage_attn_fwd_prepped", "sage_attn_fwd_prepped_kernel",
+              "sage_workspace_bytes",
               "sage_prep_scratch_bytes", "sage_debug_qk_int32", "sage_debug_codecs", "sage_debug_epoch_trace",
               "sage_status_str"):
         assert n in names
@@ -116,6 +117,11 @@ def test_prep_and_prepped_reject_bad_arguments(lib):
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 64, 0, 0.0, None) == -1
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 0, 0.0, None) == -2
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 3, 0.0, None) == -1
+    k = lib.sage_attn_fwd_prepped_kernel
+    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, 3, None) == -1   # unknown design
+    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, -1, None) == -1
+    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 64, 0, 0.0, 2, None) == -1
+    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 0, 0.0, 1, None) == -2
 
 
 def test_debug_qk_rejects_out_of_range_tiles(lib):
@@ -126,9 +132,11 @@ def test_debug_qk_rejects_out_of_range_tiles(lib):
     assert lib.sage_debug_codecs(None, 4, FAKE, FAKE, None) == -1
     t = lib.sage_debug_epoch_trace
     ok = [FAKE] * 7 + [2, 3, 128, 128, 64, 1, 0.0]
-    assert t(*ok, 2, 0, 0, FAKE, FAKE, FAKE, None) == -1       # b out of range
-    assert t(*ok, 0, 3, 0, FAKE, FAKE, FAKE, None) == -1       # h out of range
-    assert t(*ok, 0, 0, 16, FAKE, FAKE, FAKE, None) == -1      # row0 not a multiple of 32
-    assert t(*ok, 0, 0, 128, FAKE, FAKE, FAKE, None) == -1     # row0 >= Lq
-    assert t(*ok, 0, 0, 0, None, FAKE, FAKE, None) == -1       # missing output
+    assert t(*ok, 1, 2, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1       # b out of range
+    assert t(*ok, 1, 0, 3, 0, FAKE, FAKE, FAKE, FAKE, None) == -1       # h out of range
+    assert t(*ok, 2, 0, 0, 16, FAKE, FAKE, FAKE, FAKE, None) == -1      # row0 not a multiple of 32
+    assert t(*ok, 1, 0, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == -1     # row0 >= Lq
+    assert t(*ok, 1, 0, 0, 0, None, FAKE, FAKE, FAKE, None) == -1       # missing stats
+    assert t(*ok, 2, 0, 0, 0, FAKE, FAKE, None, FAKE, None) == -1       # missing pv
+    assert t(*ok, 5, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1       # unknown design
     assert lib.sage_debug_codecs(FAKE, 0, FAKE, FAKE, None) == 0

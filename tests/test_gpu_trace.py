@@ -1,6 +1,7 @@
 """Per-epoch checkpoints of the main loop against the oracle's own (Experiment
 Log, "Phase 2B Fixed Aligned Numerical Prototype": the m, d, FP8 probability,
-rescale, FP32 RO and reciprocal checkpoints, here after every epoch).
+rescale, PV, FP32 RO and reciprocal checkpoints, here after every epoch), for
+each main-loop design.
 
 sage_debug_epoch_trace runs the main kernel itself on one tile and records the
 state of 32 rows after each epoch it computes. Against oracle.attn_row_trace
@@ -11,6 +12,16 @@ on the same bf16 inputs:
   P8     the same E4M3 byte, except where exp and exp2 round a p across a
          code boundary: such bytes differ by one code and are at most 1e-3
          of the bytes compared;
+  PV     the epoch's own partial against sum_j dec(P8_j) dec(V8[j, c])
+         taken exactly (fp64) over the GPU's own P bytes, and against the
+         oracle's fp32 PV where the P bytes agree. The FP8 matrix-core step
+         does not round like an fp32 sum: it adds groups of products in a
+         fixed-point window aligned to the largest one and drops bits about
+         14 places below it (a probe of the instruction on 4824 vectors of
+         E4M3 codes: worst error 4.7e-4 of the largest product, exact for
+         products within that window). That is the precision of the pages'
+         own FP16 inner partial. Bound: 2^-9 of the channel's largest
+         |product| (4x the worst measured) plus 2^-20 of sum |products|;
   RO     fp32 sums of exact fp8 products in another order: max-abs within
          1e-3 of the epoch's largest |RO|;
 and the output rows the trace launch writes equal the main kernel's bit for
@@ -38,22 +49,28 @@ CASES = {
 }
 
 
+KERNELS = {"fused": sage.SAGE_KERNEL_FUSED, "split": sage.SAGE_KERNEL_SPLIT}
+
+
+@pytest.mark.parametrize("kernel", sorted(KERNELS))
 @pytest.mark.parametrize("wi", sorted(CASES))
-def test_epoch_checkpoints_match_the_oracle(wi, gpu_device):
+def test_epoch_checkpoints_match_the_oracle(wi, kernel, gpu_device):
     w = si.WORKLOADS[wi]
-    say(f"epoch trace: {w.name} rows {CASES[wi]}")
+    say(f"epoch trace ({kernel}): {w.name} rows {CASES[wi]}")
     q, k, v = si.workload_qkv(w)
     pr = sage.quant_prep(q.to(gpu_device), k.to(gpu_device), v.to(gpu_device))
-    full = sage.attn_fwd_prepped(pr, w.causal, w.sm_scale)
+    full = sage.attn_fwd_prepped(pr, w.causal, w.sm_scale, kernel=KERNELS[kernel])
     torch.cuda.synchronize()
     full_bits = si.bf16_bits(full)
     preps = oracle_preps(q, k, v, sorted({(b, h) for b, h, _ in CASES[wi]}))
     nkb = -(-w.Lkv // 64)
     p8_total = p8_diff = 0
     for b, h, row0 in CASES[wi]:
-        t = sage.debug_epoch_trace(pr, b, h, row0, w.causal, w.sm_scale)
+        t = sage.debug_epoch_trace(pr, b, h, row0, w.causal, w.sm_scale, kernel=KERNELS[kernel])
         torch.cuda.synchronize()
         st, p8, ro = t["stats"].cpu().numpy(), t["p8"].cpu().numpy(), t["ro"].cpu().numpy()
+        pv = t["pv"].cpu().numpy()
+        v8dec = oracle.e4m3_decode(preps[(b, h)]["v8"])  # [NKB*64, D]
         out_bits = si.bf16_bits(t["out"])
         rows = range(row0, min(row0 + 32, w.Lq))
         assert np.array_equal(out_bits[b, h, row0:rows.stop], full_bits[b, h, row0:rows.stop]), (b, h, row0)
@@ -63,6 +80,7 @@ def test_epoch_checkpoints_match_the_oracle(wi, gpu_device):
             o = oracle.attn_row_trace(preps[(b, h)], w.causal, w.sm_scale, row)
             what = f"{w.name} head ({b},{h}) row {row}"
             assert np.all(~np.isnan(st[i, :n_done, 1])) and np.all(np.isnan(st[i, n_done:nkb, 1])), what
+            assert np.all(~np.isnan(pv[i, :n_done])) and np.all(np.isnan(pv[i, n_done:nkb])), what
             for e in range(n_done):
                 mo, lo_, ao = (float(x) for x in o["stats"][e, :3])
                 mg, lg, ag = (float(x) for x in st[i, e, :3])
@@ -79,6 +97,12 @@ def test_epoch_checkpoints_match_the_oracle(wi, gpu_device):
                 scale = float(np.abs(o["ro"][e]).max())
                 err = float(np.abs(ro[i, e].astype(np.float64) - o["ro"][e]).max())
                 assert err <= 1e-3 * scale + 1e-30, (what, e, err, scale)
+                # PV: the definition over the GPU's own P bytes, then the oracle's
+                terms = oracle.e4m3_decode(p8[i, e])[:, None] * v8dec[64 * e:64 * e + 64]
+                bound = 2.0 ** -9 * np.abs(terms).max(0) + 2.0 ** -20 * np.abs(terms).sum(0) + 1e-30
+                assert np.all(np.abs(pv[i, e] - terms.sum(0)) <= bound), (what, e)
+                if not d.any():
+                    assert np.all(np.abs(pv[i, e].astype(np.float64) - o["pv"][e]) <= bound), (what, e)
             # epochs the wave did not compute change nothing in the oracle either
             for e in range(n_done, nkb):
                 assert np.array_equal(o["stats"][e, :2], o["stats"][n_done - 1, :2]) and not o["p8"][e].any(), \
