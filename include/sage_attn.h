@@ -94,6 +94,26 @@ int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, i
                     uint8_t* v_fp8, float* v_scale, void* scratch, size_t scratch_bytes, void* stream);
 
 /*
+ * sage_quant_prep for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same outputs, bit for bit, with the preparation scratch taken from a
+ * static device array of 16 MiB inside the library (one per GPU, held until
+ * the process ends) instead of a caller buffer. The call allocates nothing.
+ * Shapes whose scratch (sage_prep_scratch_bytes) exceeds 16 MiB return
+ * SAGE_ERR_WORKSPACE before any GPU call (the scratch is 12 bytes per head,
+ * 256-key split and channel: B*H*ceil(Lkv/256)*D up to about 1.39 million
+ * fits; 64 heads at Lkv = 4096 and D = 128 need 1.5 MiB). The first call
+ * on a device looks up that device's array (hipGetSymbolAddress; the current
+ * device must be the stream's device). Calls on one GPU share its array:
+ * calls whose execution overlaps on one GPU (different streams, or host
+ * threads without ordering) race and give undefined outputs; calls ordered
+ * on one stream do not.
+ */
+int sage_quant_prep_noalloc(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
+                            int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                            uint8_t* v_fp8, float* v_scale, void* stream);
+
+/*
  * Attention from prepared operands (the fused main loop alone), in the
  * layouts sage_quant_prep writes. Per query row i, strictly ascending 64-key
  * epochs (Experiment Log, "Phase 1 State-Ownership Decision"):

@@ -43,6 +43,8 @@ def lib() -> ctypes.CDLL:
                 getattr(L, n).restype = I
             L.sage_quant_prep.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]
             L.sage_quant_prep.restype = I
+            L.sage_quant_prep_noalloc.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P]
+            L.sage_quant_prep_noalloc.restype = I
             L.sage_attn_fwd_prepped.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, P]
             L.sage_attn_fwd_prepped.restype = I
             L.sage_attn_fwd_prepped_kernel.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "sage_attn.h"
 #include "sage_launch.h"
 
@@ -63,6 +65,39 @@ size_t prep_scratch(int B, int H, int Lkv, int D) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
+// Scratch of sage_quant_prep_noalloc (the preparation pass's fp64 channel
+// partial sums and fp32 channel absmax partials): a file-scope device array.
+// Each GPU holds its own copy until the process ends; every call on a GPU
+// uses that GPU's copy. In host code `scratch` only names the symbol: its
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is passed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's `scratch` (nullptr and *status set on a
+// HIP error).
+void* static_scratch(int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = SAGE_ERR_HIP;
+    return nullptr;
+  }
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *status = SAGE_ERR_HIP;
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 // The main-loop design SAGE_KERNEL_AUTO selects. When the grid has fewer
 // 128-row tiles than the GPU has compute units, the wave-specialised design
 // finishes each tile sooner (twice the waves per tile: 0.0180 against
@@ -82,18 +117,28 @@ int resolve_kernel(int kernel, int B, int H, int Lq) {
   return -1;
 }
 
+// Shapes and the input/output pointers of the preparation pass.
+int check_prep_args(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
+                    const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                    const float* k_mean, const uint8_t* v_fp8, const float* v_scale) {
+  const int st = check_dims(B, H, Lq, Lkv, D);
+  if (st != SAGE_OK) return st;
+  if (!q || !k || !v || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !v_fp8 || !v_scale)
+    return SAGE_ERR_INVALID_ARG;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(q_i8, 16) ||
+      misaligned(k_i8, 16) || misaligned(v_fp8, 16) || misaligned(q_scale, 4) || misaligned(k_scale, 4) ||
+      misaligned(k_mean, 16) || misaligned(v_scale, 16))
+    return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
 // Body of sage_quant_prep (also run by sage_attn_fwd on its workspace).
 int quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
                int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, uint8_t* v_fp8,
                float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
-  const int st = check_dims(B, H, Lq, Lkv, D);
+  const int st = check_prep_args(q, k, v, B, H, Lq, Lkv, D, q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale);
   if (st != SAGE_OK) return st;
-  if (!q || !k || !v || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !v_fp8 || !v_scale || !scratch)
-    return SAGE_ERR_INVALID_ARG;
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(q_i8, 16) ||
-      misaligned(k_i8, 16) || misaligned(v_fp8, 16) || misaligned(q_scale, 4) || misaligned(k_scale, 4) ||
-      misaligned(k_mean, 16) || misaligned(v_scale, 16) || misaligned(scratch, 8))
-    return SAGE_ERR_INVALID_ARG;
+  if (!scratch || misaligned(scratch, 8)) return SAGE_ERR_INVALID_ARG;
   if (scratch_bytes < prep_scratch(B, H, Lkv, D)) return SAGE_ERR_WORKSPACE;
   const size_t n = (size_t)B * H * sage::prep_n_split(Lkv) * D;
   sage::PrepArgs a;
@@ -171,6 +216,19 @@ int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, i
                     uint8_t* v_fp8, float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
   return quant_prep(q, k, v, B, H, Lq, Lkv, D, q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale, scratch,
                     scratch_bytes, stream);
+}
+
+int sage_quant_prep_noalloc(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
+                            int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                            uint8_t* v_fp8, float* v_scale, void* stream) {
+  const int st = check_prep_args(q, k, v, B, H, Lq, Lkv, D, q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale);
+  if (st != SAGE_OK) return st;
+  if (prep_scratch(B, H, Lkv, D) > kStaticScratchBytes) return SAGE_ERR_WORKSPACE;
+  int hs = SAGE_OK;
+  void* ws = static_scratch(&hs);
+  if (!ws) return hs;
+  return quant_prep(q, k, v, B, H, Lq, Lkv, D, q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale, ws,
+                    kStaticScratchBytes, stream);
 }
 
 int sage_attn_fwd_prepped_kernel(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,

@@ -30,7 +30,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("sage_quant_prep", "sage_attn_fwd", "sage_attn_fwd_prepped", "sage_attn_fwd_prepped_kernel",
+    for n in ("sage_quant_prep", "sage_quant_prep_noalloc", "sage_attn_fwd", "sage_attn_fwd_prepped",
+              "sage_attn_fwd_prepped_kernel",
               "sage_workspace_bytes",
               "sage_prep_scratch_bytes", "sage_debug_qk_int32", "sage_debug_codecs", "sage_debug_epoch_trace",
               "sage_status_str"):
@@ -113,6 +114,10 @@ def test_prep_and_prepped_reject_bad_arguments(lib):
     odd = list(args)
     odd[8] = ctypes.c_void_p((1 << 20) + 1)
     assert p(*odd) == -1
+    na = lib.sage_quant_prep_noalloc  # checks shapes, pointers and its 16 MiB scratch bound before any GPU call
+    assert na(FAKE, FAKE, FAKE, 1, 64, 64, 65536, 128, *([FAKE] * 7), None) == -3
+    assert na(None, FAKE, FAKE, 1, 1, 64, 64, 128, *([FAKE] * 7), None) == -1
+    assert na(FAKE, FAKE, FAKE, 1, 1, 64, 64, 96, *([FAKE] * 7), None) == -2
     a = lib.sage_attn_fwd_prepped
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 64, 0, 0.0, None) == -1
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 0, 0.0, None) == -2
