@@ -181,7 +181,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=None, help="index into seeded_inputs.WORKLOADS")
     ap.add_argument("--shape", type=str, default=None,
                     help="B,H,Lq,Lkv,D,causal: a custom N(0,1) workload (K offset sigma 2) instead of a named one")
-    ap.add_argument("--kernel", choices=("auto", "fused", "split"), default="auto",
+    ap.add_argument("--kernel", choices=("auto", "fused", "split", "persistent"), default="auto",
                     help="main-loop design timed in the main scope (sage_attn_fwd uses auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -234,8 +234,8 @@ def main() -> int:
             k8.data_ptr(), kscale.data_ptr(), kmean.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
             scratch.data_ptr(), n.value, sp))
 
-    kernel = {"auto": _lib.SAGE_KERNEL_AUTO, "fused": _lib.SAGE_KERNEL_FUSED, "split": _lib.SAGE_KERNEL_SPLIT}[
-        args.kernel]
+    kernel = {"auto": _lib.SAGE_KERNEL_AUTO, "fused": _lib.SAGE_KERNEL_FUSED, "split": _lib.SAGE_KERNEL_SPLIT,
+              "persistent": _lib.SAGE_KERNEL_PERSISTENT}[args.kernel]
 
     def main_loop():
         _lib.check("sage_attn_fwd_prepped_kernel", L.sage_attn_fwd_prepped_kernel(

@@ -15,7 +15,8 @@
  *  - q is [B][H][Lq][D], k, v are [B][H][Lkv][D], out is [B][H][Lq][D]:
  *    bf16 (raw 16-bit storage), D contiguous, base address 16-byte aligned.
  *  - D is 64 or 128; B, H, Lq, Lkv >= 1; B*H*max(Lq,Lkv)*D < 2^40, and one
- *    head's K codes fit in 2 GiB: NKB*64*D < 2^31 (Lkv < 2^24 at D = 128);
+ *    head's Q and K codes fit in 2 GiB: NQB*64*D < 2^31 and NKB*64*D < 2^31
+ *    (Lq, Lkv < 2^24 at D = 128);
  *    B*H*(NQB + 2*NKB) < 2^31 (workgroups of the preparation pass).
  *  - Quantization blocks and attention epochs are SAGE_BLOCK = 64 rows/keys;
  *    NQB = ceil(Lq/64), NKB = ceil(Lkv/64).
@@ -142,12 +143,19 @@ int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t
  *                      overlap): softmax waves hold the Q codes, scores, m
  *                      and l; PV waves hold RO; the E4M3 P block and alpha
  *                      of each epoch pass between them through LDS.
+ *   SAGE_KERNEL_PERSISTENT  the FUSED waves in persistent workgroups (as
+ *                      many as fit on the GPU at once) that take 128-row
+ *                      tiles, heaviest first, from a work counter
+ *                      (fetch-and-add). The library keeps one counter per
+ *                      stream for up to 64 streams per device (a further
+ *                      stream runs FUSED); each launch returns its counter to
+ *                      0, and calls on one stream never overlap.
  *   SAGE_KERNEL_AUTO   the design measured faster for the shape: SPLIT when
  *                      B*H*ceil(Lq/128) < 256 (fewer 128-row tiles than
  *                      compute units), FUSED otherwise. sage_attn_fwd and
  *                      sage_attn_fwd_prepped use it.
  */
-enum sage_kernel { SAGE_KERNEL_AUTO = 0, SAGE_KERNEL_FUSED = 1, SAGE_KERNEL_SPLIT = 2 };
+enum sage_kernel { SAGE_KERNEL_AUTO = 0, SAGE_KERNEL_FUSED = 1, SAGE_KERNEL_SPLIT = 2, SAGE_KERNEL_PERSISTENT = 3 };
 
 /*
  * sage_attn_fwd_prepped with an explicit main-loop design (enum

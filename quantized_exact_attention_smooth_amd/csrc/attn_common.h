@@ -113,6 +113,54 @@ __device__ __forceinline__ void v_tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int t
   }
 }
 
+// Byte offset of 16-byte chunk `chunk` of query row `row` in an LDS Q tile
+// of 128 rows x D bytes. Rows r and r + 256/D start at the same bank, so the
+// chunk index is XORed with row / (256/D): the 16 rows that one b128 read of
+// the QK step touches (rows q .. q + 15, one chunk each) then cover all 64
+// banks once.
+template <int D>
+__device__ __forceinline__ int q_swz(int row) {
+  return (row / (256 / D)) & (D / 16 - 1);
+}
+template <int D>
+__device__ __forceinline__ int q_lds_off(int row, int chunk) {
+  return row * D + ((chunk ^ q_swz<D>(row)) << 4);
+}
+
+// The 128 x D Q code tile of rows q0 .. q0 + 127 of one head, copied straight
+// into LDS (direct buffer loads; wave w of 4 copies its quarter). rsrc spans
+// the head's NQB*64 code rows: rows past them read as 0.
+template <int D>
+__device__ __forceinline__ void q_tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int q0, uint8_t* lds, int w, int lane) {
+  constexpr int kPerWave = kQTile * D / 16 / 4 / 64;
+  constexpr int kChunksPerRow = D / 16;
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int p0 = (w * kPerWave + j) * 64;
+    const int p = p0 + lane;
+    const int row = p / kChunksPerRow, pc = p % kChunksPerRow;
+    const int c = pc ^ q_swz<D>(row);  // logical chunk at physical pc
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + 16 * p0), 16, row * D + 16 * c, q0 * D, 0, 0);
+  }
+}
+
+// QK of one epoch with the Q codes read from an LDS Q tile (qoff[s]: this
+// lane's Q chunk offsets); otherwise as qk_epoch.
+template <int D>
+__device__ __forceinline__ void qk_epoch_lq(const uint8_t* lk, const uint8_t* lq, const int (&qoff)[D / 32],
+                                            const int (&koff)[D / 32], v16i& acc0, v16i& acc1) {
+  acc0 = v16i{};
+  acc1 = v16i{};
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    const v4i b = *reinterpret_cast<const v4i*>(lq + qoff[s]);
+    const v4i a0 = *reinterpret_cast<const v4i*>(lk + koff[s]);
+    const v4i a1 = *reinterpret_cast<const v4i*>(lk + koff[s] + 16 * D);
+    acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, acc1, 0, 0, 0);
+  }
+}
+
 // Pairwise exchange between lane halves: returns f(own, other) in every lane.
 // v_permlane32_swap with the same value in both operands leaves, per lane,
 // its own value in one result and the other half's value in the other.

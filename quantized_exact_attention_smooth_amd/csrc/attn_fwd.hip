@@ -65,24 +65,42 @@ namespace sage {
 template <int D, bool TRACE>
 constexpr int kWavesPerSimd = TRACE ? 1 : (D == 64 ? 4 : 3);
 
-template <int D, bool CAUSAL, bool TRACE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, TRACE>)))
-void attn_fwd_kernel(AttnArgs a) {
-  // Four separate LDS objects (not one array) so that the compiler can tell
-  // the in-flight direct fills apart from the buffers being read.
-  __shared__ __attribute__((aligned(16))) uint8_t s_k0[kBlock * D];
-  __shared__ __attribute__((aligned(16))) uint8_t s_k1[kBlock * D];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v0[D * kBlock];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v1[D * kBlock];
-  // The head's V channel scales, read at the start so that the epilogue does
-  // not wait for a global load.
-  __shared__ __attribute__((aligned(16))) float s_sv[D];
+// The LDS of one workgroup. Four separate K/V objects (not one array) so
+// that the compiler can tell the in-flight direct fills apart from the
+// buffers being read; the head's V channel scales are read at the start so
+// that the epilogue does not wait for a global load.
+template <int D>
+struct FusedLds {
+  uint8_t* k0;
+  uint8_t* k1;
+  uint8_t* v0;
+  uint8_t* v1;
+  float* sv;
+};
 
+// Work item n of the grid order: heaviest causal tile first; consecutive
+// items walk the heads, so with B*H a multiple of 8 every tile of a head
+// runs on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ void work_item(const AttnArgs& a, int n, int& tile, long& bh) {
   const int BH = a.B * a.H;
-  const int tile = TRACE ? a.trace_tile : a.n_qtiles - 1 - (int)(blockIdx.x / BH);
-  const long bh = TRACE ? (long)a.trace_bh : (long)(blockIdx.x % BH);
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  tile = a.n_qtiles - 1 - n / BH;
+  bh = n % BH;
+}
+
+// One 128-row tile of head bh.
+template <int D, bool CAUSAL, bool TRACE>
+__device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, const long bh, uint8_t* s_k0,
+                                           uint8_t* s_k1, uint8_t* s_v0, uint8_t* s_v1, uint8_t* s_q,
+                                           float* s_sv) {
+  // The thread index is made opaque here, so that the per-lane offsets
+  // derived from it are computed where they are used, in every tile, rather
+  // than hoisted out of a persistent workgroup's tile loop (where they would
+  // stay live through every epoch loop and push the kernel past its
+  // registers).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int h = lane >> 5, ql = lane & 31;
   const int q0 = tile * kQTile;
   const int wrow0 = q0 + 32 * w;
@@ -123,14 +141,17 @@ void attn_fwd_kernel(AttnArgs a) {
     v_tile_to_lds<D>(vrs, 0, s_v0, w, lane);
   }
 
-  v4i qreg[D / 32];
-  const int8_t* qh = a.q_i8 + bh * (long)a.nqb * kBlock * D;
+  // The tile's Q codes go straight into LDS with the first fills.
+  const int q_bytes = a.nqb * kBlock * D;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.q_i8 + bh * (long)q_bytes), (short)0, q_bytes, kRawBufferFlags);
+  q_tile_to_lds<D>(qrs, q0, s_q, w, lane);
+  int qoff[D / 32];
 #pragma unroll
-  for (int s = 0; s < D / 32; ++s)
-    qreg[s] = (qrow < a.Lq) ? *reinterpret_cast<const v4i*>(qh + (long)qrow * D + 32 * s + 16 * h) : v4i{};
+  for (int s = 0; s < D / 32; ++s) qoff[s] = q_lds_off<D>(32 * w + ql, 2 * s + h);
   const float sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
   const float cq = sq * a.scale_log2;
-  if (threadIdx.x < D) s_sv[threadIdx.x] = a.v_scale[bh * D + threadIdx.x];
+  if (tid < D) s_sv[tid] = a.v_scale[bh * D + tid];
 
   // The QK read offsets are computed once; the empty asm keeps the compiler
   // from rebuilding them from their parts in every epoch (four VALU adds).
@@ -160,7 +181,7 @@ void attn_fwd_kernel(AttnArgs a) {
     }
     if (e < w_ep) {
       v16i acc0, acc1;
-      qk_epoch<D>(k_cur, qreg, koff, acc0, acc1);
+      qk_epoch_lq<D>(k_cur, s_q, qoff, koff, acc0, acc1);
       // log2-domain score per unit of the int32 accumulator
       const float c = cq * ksh[e];
       const bool masked = kBlock * e + kBlock - 1 > w_lim;  // wave-uniform
@@ -202,6 +223,60 @@ void attn_fwd_kernel(AttnArgs a) {
   if (TRACE && w == a.trace_wave) trace_final(a, h, ql, rcp, lt);
   uint8_t* stage = w == 0 ? s_k0 : w == 1 ? s_k1 : w == 2 ? s_v0 : s_v1;  // 32 rows x 2D bytes
   store_rows<D>(ro, rcp, s_sv, stage, a.out, bh, a.Lq, wrow0, lane, h, ql);
+}
+
+template <int D, bool CAUSAL, bool TRACE, bool PERSIST>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, TRACE>)))
+void attn_fwd_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_k0[kBlock * D];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k1[kBlock * D];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v0[D * kBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v1[D * kBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[kQTile * D];
+  __shared__ __attribute__((aligned(16))) float s_sv[D];
+  if (TRACE) {
+    fused_tile<D, CAUSAL, TRACE>(a, a.trace_tile, a.trace_bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    return;
+  }
+  if (!PERSIST) {
+    int tile;
+    long bh;
+    work_item(a, blockIdx.x, tile, bh);
+    fused_tile<D, CAUSAL, TRACE>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    return;
+  }
+  // Persistent workgroups take work items from counters (fetch-and-add), one
+  // per XCD: workgroups are dealt to the 8 XCDs round-robin, so workgroup b
+  // runs on XCD x = b % 8 and takes the items n = x + 8 k, k = 0, 1, ... in
+  // order (heaviest first), as the per-tile grid would place them: with B*H a
+  // multiple of 8, every tile of a head then stays on one XCD and its L2.
+  // Each workgroup's last fetch is past the end, so counter x serves exactly
+  // items_x + wgs_x fetches in a launch; the workgroup that draws the last
+  // of them returns it to 0 for the next launch on this counter (no other
+  // workgroup of the launch touches that counter afterwards).
+  __shared__ int s_item;
+  constexpr int kXcds = 8;
+  const int n_items = a.n_qtiles * a.B * a.H;
+  const int x = blockIdx.x % kXcds;
+  const int items_x = (n_items - x + kXcds - 1) / kXcds;
+  const int wgs_x = ((int)gridDim.x - x + kXcds - 1) / kXcds;
+  unsigned int* queue = a.queue + x;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = (int)atomicAdd(queue, 1u);
+    __syncthreads();
+    const int k = s_item;
+    if (k >= items_x) {
+      if (threadIdx.x == 0 && k == items_x + wgs_x - 1) atomicExch(queue, 0u);
+      return;
+    }
+    int tile;
+    long bh;
+    work_item(a, x + kXcds * k, tile, bh);
+    fused_tile<D, CAUSAL, TRACE>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    // Every wave is done with the LDS (the epilogue staged its rows in the
+    // K/V buffers) and with s_item before the next item refills them.
+    __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------ debug kernels
@@ -265,26 +340,31 @@ __global__ __launch_bounds__(256) void codecs_debug_kernel(const float* __restri
 
 // ------------------------------------------------------------ launchers
 
-template <int D, bool C, bool T>
+template <int D, bool C, bool T, bool P>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
-  const long blocks = T ? 1L : (long)a.n_qtiles * a.B * a.H;
-  attn_fwd_kernel<D, C, T><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
+  const long blocks = T ? 1L : P ? (long)a.persist_grid : (long)a.n_qtiles * a.B * a.H;
+  attn_fwd_kernel<D, C, T, P><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <bool T>
+template <bool T, bool P>
 static hipError_t launch_attn_v(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  if (D == 128) return causal ? launch_attn_t<128, true, T>(a, stream) : launch_attn_t<128, false, T>(a, stream);
-  return causal ? launch_attn_t<64, true, T>(a, stream) : launch_attn_t<64, false, T>(a, stream);
+  if (D == 128)
+    return causal ? launch_attn_t<128, true, T, P>(a, stream) : launch_attn_t<128, false, T, P>(a, stream);
+  return causal ? launch_attn_t<64, true, T, P>(a, stream) : launch_attn_t<64, false, T, P>(a, stream);
 }
 
 hipError_t launch_attn_fused(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream) {
-  return trace ? launch_attn_v<true>(a, D, causal, stream) : launch_attn_v<false>(a, D, causal, stream);
+  return trace ? launch_attn_v<true, false>(a, D, causal, stream) : launch_attn_v<false, false>(a, D, causal, stream);
+}
+hipError_t launch_attn_persistent(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
+  return launch_attn_v<false, true>(a, D, causal, stream);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream) {
-  return kernel == kKernelSplit ? launch_attn_split(a, D, causal, false, stream)
-                                : launch_attn_fused(a, D, causal, false, stream);
+  if (kernel == kKernelSplit) return launch_attn_split(a, D, causal, false, stream);
+  if (kernel == kKernelPersistent) return launch_attn_persistent(a, D, causal, stream);
+  return launch_attn_fused(a, D, causal, false, stream);
 }
 hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream) {
   return kernel == kKernelSplit ? launch_attn_split(a, D, causal, true, stream)

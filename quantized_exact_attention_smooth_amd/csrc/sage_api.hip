@@ -29,9 +29,12 @@ int check_dims(int B, int H, int Lq, int Lkv, int D) {
   if ((double)B * H * (nqb + 2 * nkb) >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
   if ((double)B * H * sage::prep_n_split(Lkv) >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
   if ((double)B * H * (D / 32) >= 2147483647.0) return SAGE_ERR_INVALID_ARG;
-  // The main loop addresses one head's K or V codes with 32-bit buffer offsets.
+  // The main loop addresses one head's Q, K or V codes with 32-bit buffer
+  // offsets.
   const double head_codes = (double)((Lkv + sage::kBlock - 1) / sage::kBlock) * sage::kBlock * D;
   if (head_codes >= 2147483648.0) return SAGE_ERR_INVALID_ARG;
+  const double head_q = (double)((Lq + sage::kBlock - 1) / sage::kBlock) * sage::kBlock * D;
+  if (head_q >= 2147483648.0) return SAGE_ERR_INVALID_ARG;
   return SAGE_OK;
 }
 
@@ -76,6 +79,51 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 constexpr int kMaxDevices = 64;
 
+// Work counters of the persistent main-loop design: one set of 8 (one per
+// XCD) per stream that has used it (calls on one stream run in order, so a
+// set never serves two launches at once). Every launch leaves its counters at
+// 0.
+constexpr int kQueueSlots = 64;
+constexpr int kQueuesPerSlot = 8;  // one counter per XCD
+static __device__ unsigned int work_queue[kQueueSlots * kQueuesPerSlot];
+
+struct QueueTable {
+  unsigned int* base = nullptr;  // device address of work_queue
+  int cus = 0;                   // compute units
+  void* streams[kQueueSlots] = {};
+  int used = 0;
+};
+
+// This device's counter for `stream` and its compute-unit count; nullptr when
+// every slot is taken by other streams (the caller then runs the
+// non-persistent design) or on a HIP error (*status set).
+unsigned int* queue_for(void* stream, int* cus, int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = SAGE_ERR_HIP;
+    return nullptr;
+  }
+  static std::mutex mu;
+  static QueueTable table[kMaxDevices];
+  std::lock_guard<std::mutex> lock(mu);
+  QueueTable& t = table[dev];
+  if (!t.base) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(work_queue)) != hipSuccess || !p ||
+        hipDeviceGetAttribute(&t.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      *status = SAGE_ERR_HIP;
+      return nullptr;
+    }
+    t.base = (unsigned int*)p;
+  }
+  *cus = t.cus;
+  for (int i = 0; i < t.used; ++i)
+    if (t.streams[i] == stream) return t.base + kQueuesPerSlot * i;
+  if (t.used == kQueueSlots) return nullptr;
+  t.streams[t.used] = stream;
+  return t.base + kQueuesPerSlot * t.used++;
+}
+
 // Device address of this device's `scratch` (nullptr and *status set on a
 // HIP error).
 void* static_scratch(int* status) {
@@ -114,6 +162,7 @@ int resolve_kernel(int kernel, int B, int H, int Lq) {
   if (kernel == SAGE_KERNEL_AUTO) return auto_kernel(B, H, Lq);
   if (kernel == SAGE_KERNEL_FUSED) return sage::kKernelFused;
   if (kernel == SAGE_KERNEL_SPLIT) return sage::kKernelSplit;
+  if (kernel == SAGE_KERNEL_PERSISTENT) return sage::kKernelPersistent;
   return -1;
 }
 
@@ -218,6 +267,24 @@ int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, i
                     scratch_bytes, stream);
 }
 
+// Counter and grid of a persistent launch: one workgroup per resident slot
+// (three per compute unit at D = 128, four at D = 64), at most one per work
+// item. Falls back to the non-persistent design (*kind) when no counter is
+// free for the stream; false on a HIP error.
+bool persistent_setup(sage::AttnArgs* a, int D, void* stream, int* kind) {
+  int cus = 0, st = SAGE_OK;
+  a->queue = queue_for(stream, &cus, &st);
+  if (st != SAGE_OK) return false;
+  if (!a->queue) {
+    *kind = sage::kKernelFused;
+    return true;
+  }
+  const long items = (long)a->n_qtiles * a->B * a->H;
+  const long slots = (long)cus * (D == 64 ? 4 : 3);
+  a->persist_grid = (int)(items < slots ? items : slots);
+  return true;
+}
+
 int sage_quant_prep_noalloc(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
                             int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
                             uint8_t* v_fp8, float* v_scale, void* stream) {
@@ -239,8 +306,9 @@ int sage_attn_fwd_prepped_kernel(const int8_t* q_i8, const float* q_scale, const
   const int st = attn_args(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, out, B, H, Lq, Lkv, D, causal,
                            sm_scale, &a);
   if (st != SAGE_OK) return st;
-  const int kind = resolve_kernel(kernel, B, H, Lq);
+  int kind = resolve_kernel(kernel, B, H, Lq);
   if (kind < 0) return SAGE_ERR_INVALID_ARG;
+  if (kind == sage::kKernelPersistent && !persistent_setup(&a, D, stream, &kind)) return SAGE_ERR_HIP;
   return hip_status(sage::launch_attn(a, D, causal == 1, kind, (hipStream_t)stream));
 }
 

@@ -46,6 +46,10 @@ struct AttnArgs {
   uint8_t* tr_p8;
   float* tr_ro;
   float* tr_pv;
+  // Persistent design: the launch-wide work counter (0 when a launch starts;
+  // each launch leaves it at 0) and the number of workgroups.
+  unsigned int* queue;
+  int persist_grid;
 };
 
 constexpr int kMaxDebugTiles = 64;
@@ -60,6 +64,7 @@ struct QkDebugArgs {
 // Main-loop kernel designs (the values of SAGE_KERNEL_* in sage_attn.h).
 constexpr int kKernelFused = 1;  // every wave runs QK, softmax and PV for its rows
 constexpr int kKernelSplit = 2;  // softmax waves and PV waves own separate state
+constexpr int kKernelPersistent = 3;  // fused waves in persistent workgroups fed by a work counter
 
 int prep_n_split(int Lkv);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);

@@ -1,0 +1,132 @@
+"""The other main-loop designs against the oracle and against the fused
+design: the wave-specialised one (SAGE_KERNEL_SPLIT) and the persistent one
+(SAGE_KERNEL_PERSISTENT, fused waves in workgroups fed by a work counter).
+
+Every design runs the same per-epoch arithmetic in the same order (the same
+P bytes, the same rescale and matrix-core accumulation of RO, the same
+epilogue), so their outputs must agree bit for bit on every shape; each is
+also checked against the oracle directly, to the output bar (max-abs 2e-2,
+mean-abs 2e-3 per head or block).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+import quantized_exact_attention_smooth_amd as sage
+from _parity import assert_out_close, oracle_preps, oracle_rows, say
+
+pytestmark = pytest.mark.gpu
+
+FUSED = sage.SAGE_KERNEL_FUSED
+DESIGNS = {"split": sage.SAGE_KERNEL_SPLIT, "persistent": sage.SAGE_KERNEL_PERSISTENT}
+
+
+@pytest.fixture(params=sorted(DESIGNS))
+def design(request):
+    return DESIGNS[request.param]
+
+
+def _both(q, k, v, causal, sm_scale, dev, design):
+    pr = sage.quant_prep(q.to(dev), k.to(dev), v.to(dev))
+    a = sage.attn_fwd_prepped(pr, causal, sm_scale, kernel=FUSED)
+    b = sage.attn_fwd_prepped(pr, causal, sm_scale, kernel=design)
+    torch.cuda.synchronize()
+    return si.bf16_bits(a), si.bf16_bits(b)
+
+
+SHAPES = [(1, 1, 1, 1, 64, False), (1, 1, 1, 1, 128, True), (1, 2, 63, 63, 64, True), (1, 1, 64, 64, 128, False),
+          (1, 1, 65, 65, 128, True), (1, 2, 127, 129, 64, False), (1, 1, 129, 127, 128, True),
+          (2, 3, 200, 333, 128, True), (1, 1, 1000, 64, 64, True), (1, 1, 64, 1000, 128, True),
+          (1, 1, 191, 193, 64, False), (1, 2, 300, 300, 128, True), (1, 1, 257, 1, 128, False),
+          (1, 1, 384, 384, 64, True), (1, 1, 130, 190, 128, False), (1, 1, 200, 64, 128, True)]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lkv,D,causal", SHAPES)
+def test_design_equals_fused_and_oracle_on_edge_shapes(B, H, Lq, Lkv, D, causal, design, gpu_device):
+    say(f"design {design} vs fused vs oracle: shape {(B, H, Lq, Lkv, D, causal)}")
+    q, k, v = si.make_qkv(B, H, Lq, Lkv, D, "normal", 2.0, seed=Lq * 5 + Lkv + D)
+    sc = 1 / math.sqrt(D)
+    fused, split = _both(q, k, v, causal, sc, gpu_device, design)
+    assert np.array_equal(fused, split)
+    for (b, h), o in oracle_preps(q, k, v, [(b, h) for b in range(B) for h in range(H)]).items():
+        assert_out_close(split[b, h], oracle_rows(o, causal, sc, 0, Lq), f"split head {(b, h)}")
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_design_small_workloads_against_oracle(idx, design, gpu_device):
+    w = si.WORKLOADS[idx]
+    say(f"design {design} vs oracle (all rows): {w.name}")
+    q, k, v = si.workload_qkv(w)
+    fused, split = _both(q, k, v, w.causal, w.sm_scale, gpu_device, design)
+    assert np.array_equal(fused, split)
+    for (b, h), o in oracle_preps(q, k, v, si.oracle_heads(w)).items():
+        assert_out_close(split[b, h], oracle_rows(o, w.causal, w.sm_scale, 0, w.Lq), f"{w.name} head {(b, h)}")
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_design_equals_fused_on_full_size_workloads(idx, design, gpu_device):
+    """Bit-identical to the fused design at full size (whose oracle parity on
+    the seeded subsets is tested in test_gpu_attn); one seeded block is also
+    checked against the oracle directly."""
+    w = si.WORKLOADS[idx]
+    say(f"design {design} vs fused (full size): {w.name}")
+    q, k, v = si.workload_qkv(w)
+    fused, split = _both(q, k, v, w.causal, w.sm_scale, gpu_device, design)
+    assert np.array_equal(fused, split)
+    b, h, qb = si.oracle_blocks(w)[-1] if w.oracle_subset[0] == "blocks" else (*si.oracle_heads(w)[0], w.Lq // 64 - 1)
+    r0, r1 = 64 * qb, min(w.Lq, 64 * qb + 64)
+    o = oracle_preps(q, k, v, [(b, h)])[(b, h)]
+    assert_out_close(split[b, h, r0:r1], oracle_rows(o, w.causal, w.sm_scale, r0, r1), f"{w.name} {(b, h, qb)}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_design_equals_fused_on_seeded_random_shapes(seed, design, gpu_device):
+    r = np.random.default_rng(1000 + seed)
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
+    Lq, Lkv = int(r.integers(1, 700)), int(r.integers(1, 700))
+    D = int(r.choice([64, 128]))
+    causal = bool(r.integers(0, 2))
+    dist = "student_t_outlier" if seed % 3 == 2 else "normal"
+    say(f"design {design} vs fused: seed {seed} shape {(B, H, Lq, Lkv, D, causal)} {dist}")
+    q, k, v = si.make_qkv(B, H, Lq, Lkv, D, dist, 3.0, seed=77 + seed)
+    fused, split = _both(q, k, v, causal, 1 / math.sqrt(D), gpu_device, design)
+    assert np.array_equal(fused, split)
+
+
+def test_design_repeated_launches_are_bit_identical(design, gpu_device):
+    w = si.WORKLOADS[2]
+    q, k, v = si.workload_qkv(w)
+    pr = sage.quant_prep(q.to(gpu_device), k.to(gpu_device), v.to(gpu_device))
+    first = si.bf16_bits(sage.attn_fwd_prepped(pr, w.causal, w.sm_scale, kernel=design))
+    out = torch.empty((w.B, w.H, w.Lq, w.D), dtype=torch.bfloat16, device=gpu_device)
+    for i in range(50):
+        sage.attn_fwd_prepped(pr, w.causal, w.sm_scale, out=out, kernel=design)
+    torch.cuda.synchronize()
+    assert np.array_equal(si.bf16_bits(out), first)
+
+
+def test_persistent_counter_returns_to_zero_across_streams_and_shapes(gpu_device):
+    """Launches of the persistent design alternate shapes (grids smaller than,
+    equal to and larger than the resident workgroup count) and two streams;
+    each must leave its stream's counter at 0 for the next, so every output
+    equals the fused design's."""
+    s2 = torch.cuda.Stream()
+    cases = [(1, 1, 128, 192, 128, False), (2, 32, 4096, 4096, 128, True), (1, 2, 1000, 700, 64, True),
+             (4, 16, 2048, 2048, 64, True)]
+    preps, refs = [], []
+    for i, (B, H, Lq, Lkv, D, causal) in enumerate(cases):
+        q, k, v = si.make_qkv(B, H, Lq, Lkv, D, "normal", 2.0, seed=300 + i)
+        pr = sage.quant_prep(q.to(gpu_device), k.to(gpu_device), v.to(gpu_device))
+        preps.append((pr, causal))
+        refs.append(si.bf16_bits(sage.attn_fwd_prepped(pr, causal, None, kernel=FUSED)))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, (pr, causal) in enumerate(preps):
+            st = s2 if (i + rep) % 2 else torch.cuda.current_stream()
+            with torch.cuda.stream(st):
+                o = sage.attn_fwd_prepped(pr, causal, None, kernel=sage.SAGE_KERNEL_PERSISTENT)
+            st.synchronize()
+            assert np.array_equal(si.bf16_bits(o), refs[i]), (rep, i)
