@@ -19,7 +19,11 @@ JSON line.
   cpu_baseline  the CPU oracle (prep + epoch loop) on a bounded sample: one
             full (b, h) head, rows spread over the host cores, with the
             full-workload time extrapolated from it; the brute-force fp64
-            reference is timed beside it on the first rows of that head.
+            reference is timed beside it on the first rows of that head;
+  accuracy  on that head: the GPU path against the oracle (max-abs and
+            mean-abs, bar 2e-2 / 2e-3) and both against fp64 attention
+            (cosine, bar 0.995), with the oracle's measured minimum cosine
+            per workload (the Student-t outlier workload misses the bar).
 """
 from __future__ import annotations
 
@@ -65,43 +69,94 @@ def _src_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str):
-    """HBM bytes per main-kernel launch from the committed counter summary,
-    only if it was taken on the current kernel sources."""
+def _profile(workload: str) -> dict:
+    """The committed counter summary of the main kernel on this workload
+    (HBM bytes per launch, matrix-core and VALU busy fractions), only if it
+    was taken on the current kernel sources; {} otherwise."""
     p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm.json")
     if not os.path.exists(p):
-        return None
+        return {}
     with open(p) as f:
         d = json.load(f)
-    if d.get("src_hash") != _src_hash():
-        return None
-    return d.get("bytes_per_launch")
+    return d if d.get("src_hash") == _src_hash() else {}
 
 
-def cpu_baseline(w) -> dict:
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Minimum cosine of the oracle's output against brute-force fp64 attention of
+# the same bf16 inputs on each workload's oracle subset, as
+# tests/test_oracle_workloads.py measures it (the accuracy bar is 0.995).
+ORACLE_MIN_COSINE = {
+    "q128_kv192_d128": 0.99935,
+    "ragged_causal_b1_h8_l1000_d128": 0.99926,
+    "causal_b2_h32_l4096_d128": 0.99919,
+    "long_b1_h24_l32760_d128": 0.99913,
+    "outlier_causal_b4_h16_l8192_d64": 0.91827,
+}
+COSINE_BAR = 0.995
+
+
+def _cos(a, b) -> float:
     import numpy as np
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / math.sqrt((a @ a) * (b @ b)))
+
+
+def cpu_baseline(w, dev) -> tuple:
+    """The oracle on one seeded (b, h) head of the workload's shape, timed on
+    the host cores; returns (cpu_baseline, accuracy): the accuracy record
+    compares, on that head, the oracle with fp64 attention (first rows) and
+    the GPU path (sage_attn_fwd) with both."""
+    import numpy as np
+    import torch
     import oracle
     import seeded_inputs as si
+    import quantized_exact_attention_smooth_amd as sage
 
     threads = oracle.default_threads()
     q, k, v = si.make_qkv(1, 1, w.Lq, w.Lkv, w.D, w.dist, w.k_offset_sigma, seed=1000)
     qb, kb, vb = (si.bf16_bits(t[0, 0]) for t in (q, k, v))
     t0 = time.perf_counter()
     p = oracle.prep_head(qb, kb, vb)
-    oracle.attn_rows_parallel(p, w.causal, w.sm_scale, 0, w.Lq, threads=threads, chunk=64)
+    orc = oracle.attn_rows_parallel(p, w.causal, w.sm_scale, 0, w.Lq, threads=threads, chunk=64)
     dt = time.perf_counter() - t0
     ops = 4.0 * w.Lq * w.Lkv * w.D / (2 if w.causal else 1)
     # brute-force fp64 reference on the first rows of the same head
     n_ref = min(w.Lq, 1024)
     qf, kf, vf = (oracle.bf16_to_f32(b).astype(np.float64) for b in (qb, kb, vb))
     t1 = time.perf_counter()
-    oracle.attn_ref_parallel(qf, kf, vf, w.causal, w.sm_scale, 0, n_ref, threads=threads, chunk=64)
+    ref = oracle.attn_ref_parallel(qf, kf, vf, w.causal, w.sm_scale, 0, n_ref, threads=threads, chunk=64)
     dt_ref = time.perf_counter() - t1
-    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+    base = {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"one (b,h) head of {w.name}: preparation + all {w.Lq} query rows, "
                       f"{dt:.2f} s wall on {threads} threads",
             "full_workload_s_extrapolated": dt * w.B * w.H,
             "fp64_reference": {"rows": n_ref, "s": dt_ref}}
+    gpu = si.bf16_bits(sage.attn_fwd(q.to(dev), k.to(dev), v.to(dev), w.causal, w.sm_scale))[0, 0]
+    torch.cuda.synchronize()
+    g, o = oracle.bf16_to_f32(gpu).astype(np.float64), oracle.bf16_to_f32(orc).astype(np.float64)
+    d = np.abs(g - o)
+    acc = {"sample": f"the cpu_baseline head: GPU vs oracle on all {w.Lq} rows, both vs fp64 attention on the "
+                     f"first {n_ref} rows",
+           "gpu_vs_oracle_max_abs": float(d.max()), "gpu_vs_oracle_mean_abs": float(d.mean()),
+           "gpu_vs_oracle_bar": {"max_abs": 2e-2, "mean_abs": 2e-3},
+           "oracle_vs_fp64_cosine": _cos(o[:n_ref], ref), "gpu_vs_fp64_cosine": _cos(g[:n_ref], ref),
+           "cosine_bar": COSINE_BAR,
+           "oracle_min_cosine_by_workload": {
+               name: {"min_cosine": c, "meets_bar": c >= COSINE_BAR} for name, c in ORACLE_MIN_COSINE.items()},
+           "oracle_min_cosine_source": "tests/test_oracle_workloads.py on each workload's oracle subset"}
+    return base, acc
 
 
 # The one timing the pages print for this method: the fast attention kernel of
@@ -183,6 +238,8 @@ def main() -> int:
                     help="B,H,Lq,Lkv,D,causal: a custom N(0,1) workload (K offset sigma 2) instead of a named one")
     ap.add_argument("--kernel", choices=("auto", "fused", "split", "persistent"), default="auto",
                     help="main-loop design timed in the main scope (sage_attn_fwd uses auto)")
+    ap.add_argument("--single-samples", type=int, default=2000,
+                    help="single launches timed for the main kernel's single-launch p50 (fewer under a profiler)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration only: time a plain device copy of this many bytes and exit")
@@ -301,7 +358,7 @@ def main() -> int:
         e1.record(stream)
         e1.synchronize()
         batches.append(e0.elapsed_time(e1) / 20)
-    n_single = 2000 if main_avg < 1.0 else 50
+    n_single = args.single_samples if main_avg < 1.0 else min(args.single_samples, 50)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_single)]
     for e0, e1 in ev:
         e0.record(stream)
@@ -315,6 +372,8 @@ def main() -> int:
     ms_step = wall * 1e3 / K
     ops = w.metric_ops
     achieved = ops / (main_avg * 1e-3) / 1e12
+    prof = _profile(w.name)
+    traffic = prof.get("bytes_per_launch")
     prep_bytes = B * H * (Lq + 2 * Lkv) * D * 2 + B * H * (nqb + 2 * nkb) * 64 * D
 
     rec = {
@@ -323,8 +382,13 @@ def main() -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "int8+fp8_e4m3", "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "Lq": Lq, "Lkv": Lkv, "D": D, "causal": w.causal,
                    "k_offset_sigma": w.k_offset_sigma, "dist": w.dist, "main_kernel": args.kernel},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_TOPS, "traffic": _traffic(w.name)},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TOPS",
+                     "frac": achieved / PEAK_TOPS, "traffic": traffic,
+                     "scope": "main kernel (sage_attn_fwd_prepped); value is the whole step",
+                     "e2e_frac": ops / (e2e_avg * 1e-3) / 1e12 / PEAK_TOPS,
+                     "hbm_GBps": traffic / (main_avg * 1e-3) / 1e9 if traffic else None,
+                     "mfma_busy": prof.get("mfma_busy"), "valu_busy": prof.get("valu_busy"),
+                     "counters": "profiles/attn_fwd_%s.md" % w.name if prof else None},
         "main_ms": main_avg, "main_tops": achieved,
         "settle_steps": settle,
         "main_batched_p50_ms": (bsorted[4] + bsorted[5]) / 2, "main_batched_cv": b_cv,
@@ -336,7 +400,7 @@ def main() -> int:
     if args.workload is None and not args.shape:
         rec["fixture_q128_kv192"] = fixture_latency(L, dev, stream)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w)
+        rec["cpu_baseline"], rec["accuracy"] = cpu_baseline(w, dev)
     print(json.dumps(rec), flush=True)
     return 0
 

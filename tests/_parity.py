@@ -62,8 +62,20 @@ def out_errors(gpu_bits, orc_bits):
     return float(d.max()), float(d.mean())
 
 
+# Worst output margins seen per comparison label in this session (label ->
+# [max-abs, mean-abs, comparisons]); conftest prints them at the end.
+MARGINS = {}
+
+
+def _label(what):
+    """Group comparisons by their workload or shape (drop head/row indices)."""
+    return what.split(" (")[0].split(" head")[0].strip() or "unlabelled"
+
+
 def assert_out_close(gpu_bits, orc_bits, what=""):
     mx, mean = out_errors(gpu_bits, orc_bits)
+    m = MARGINS.setdefault(_label(what), [0.0, 0.0, 0])
+    m[0], m[1], m[2] = max(m[0], mx), max(m[1], mean), m[2] + 1
     assert np.all(np.isfinite(oracle.bf16_to_f32(gpu_bits))), f"{what}: non-finite output"
     assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{what}: max-abs {mx:.3e} mean-abs {mean:.3e}"
     return mx, mean

@@ -77,7 +77,7 @@ def test_ragged_and_edge_shapes(B, H, Lq, Lkv, D, causal, gpu_device):
     out = _gpu_out(q, k, v, causal, sc, gpu_device)
     for (b, h), o in oracle_preps(q, k, v, [(b, h) for b in range(B) for h in range(H)]).items():
         ref = oracle_rows(o, causal, sc, 0, Lq)
-        assert_out_close(out[b, h], ref, f"head {(b, h)}")
+        assert_out_close(out[b, h], ref, f"edge and ragged shapes head {(b, h)}")
         if causal and Lq > Lkv:
             assert np.all(out[b, h, :Lq - Lkv] == 0)
 
@@ -209,7 +209,7 @@ def test_more_heads_than_a_grid_dimension_holds(gpu_device):
             src = (b * H + h) % period
             o = oracle.prep_head(si.bf16_bits(q0[0, src]), si.bf16_bits(k0[0, src]), si.bf16_bits(v0[0, src]))
             assert_prep_equal(g, o, b, j)
-            assert_out_close(out[b, h], oracle.attn_rows(o, True, 0.125), f"head ({b},{h})")
+            assert_out_close(out[b, h], oracle.attn_rows(o, True, 0.125), f"many heads (B*H beyond a grid dimension): head ({b},{h})")
 
 
 def _random_shapes(n=24, seed=20261202):
@@ -238,7 +238,7 @@ def test_seeded_random_shapes(B, H, Lq, Lkv, D, causal, dist, sigma, seed, gpu_d
     g = gpu_prep_numpy(p)
     for (b, h), o in oracle_preps(q, k, v, [(b, h) for b in range(B) for h in range(H)]).items():
         assert_prep_equal(g, o, b, h)
-        assert_out_close(out[b, h], oracle_rows(o, causal, sc, 0, Lq), f"head {(b, h)}")
+        assert_out_close(out[b, h], oracle_rows(o, causal, sc, 0, Lq), f"seeded random shapes head {(b, h)}")
 
 
 def _times_pow2(t: torch.Tensor, e: int) -> torch.Tensor:

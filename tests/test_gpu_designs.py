@@ -52,7 +52,7 @@ def test_design_equals_fused_and_oracle_on_edge_shapes(B, H, Lq, Lkv, D, causal,
     fused, split = _both(q, k, v, causal, sc, gpu_device, design)
     assert np.array_equal(fused, split)
     for (b, h), o in oracle_preps(q, k, v, [(b, h) for b in range(B) for h in range(H)]).items():
-        assert_out_close(split[b, h], oracle_rows(o, causal, sc, 0, Lq), f"split head {(b, h)}")
+        assert_out_close(split[b, h], oracle_rows(o, causal, sc, 0, Lq), f"designs: edge shapes head {(b, h)}")
 
 
 @pytest.mark.parametrize("idx", [0, 1])
@@ -63,7 +63,7 @@ def test_design_small_workloads_against_oracle(idx, design, gpu_device):
     fused, split = _both(q, k, v, w.causal, w.sm_scale, gpu_device, design)
     assert np.array_equal(fused, split)
     for (b, h), o in oracle_preps(q, k, v, si.oracle_heads(w)).items():
-        assert_out_close(split[b, h], oracle_rows(o, w.causal, w.sm_scale, 0, w.Lq), f"{w.name} head {(b, h)}")
+        assert_out_close(split[b, h], oracle_rows(o, w.causal, w.sm_scale, 0, w.Lq), f"designs: {w.name} head {(b, h)}")
 
 
 @pytest.mark.parametrize("idx", [2, 3, 4])
@@ -79,7 +79,7 @@ def test_design_equals_fused_on_full_size_workloads(idx, design, gpu_device):
     b, h, qb = si.oracle_blocks(w)[-1] if w.oracle_subset[0] == "blocks" else (*si.oracle_heads(w)[0], w.Lq // 64 - 1)
     r0, r1 = 64 * qb, min(w.Lq, 64 * qb + 64)
     o = oracle_preps(q, k, v, [(b, h)])[(b, h)]
-    assert_out_close(split[b, h, r0:r1], oracle_rows(o, w.causal, w.sm_scale, r0, r1), f"{w.name} {(b, h, qb)}")
+    assert_out_close(split[b, h, r0:r1], oracle_rows(o, w.causal, w.sm_scale, r0, r1), f"designs: {w.name} {(b, h, qb)}")
 
 
 @pytest.mark.parametrize("seed", range(6))
