@@ -78,15 +78,6 @@ struct FusedLds {
   float* sv;
 };
 
-// Work item n of the grid order: heaviest causal tile first; consecutive
-// items walk the heads, so with B*H a multiple of 8 every tile of a head
-// runs on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
-__device__ __forceinline__ void work_item(const AttnArgs& a, int n, int& tile, long& bh) {
-  const int BH = a.B * a.H;
-  tile = a.n_qtiles - 1 - n / BH;
-  bh = n % BH;
-}
-
 // One 128-row tile of head bh.
 template <int D, bool CAUSAL, bool TRACE>
 __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, const long bh, uint8_t* s_k0,

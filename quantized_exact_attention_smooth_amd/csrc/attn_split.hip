@@ -60,9 +60,9 @@ void attn_split_kernel(AttnArgs a) {
   __shared__ float s_rcp[4 * 32];  // 1/l per row, for the epilogue
   __shared__ __attribute__((aligned(16))) float s_sv[D];
 
-  const int BH = a.B * a.H;
-  const int tile = TRACE ? a.trace_tile : a.n_qtiles - 1 - (int)(blockIdx.x / BH);
-  const long bh = TRACE ? (long)a.trace_bh : (long)(blockIdx.x % BH);
+  int tile = a.trace_tile;
+  long bh = a.trace_bh;
+  if (!TRACE) work_item(a, blockIdx.x, tile, bh);
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = wid & 3;                                              // row group

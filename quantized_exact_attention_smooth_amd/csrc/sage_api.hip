@@ -226,6 +226,7 @@ int attn_args(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, cons
   a->nkb = (Lkv + sage::kBlock - 1) / sage::kBlock;
   a->n_qtiles = (Lq + sage::kQTile - 1) / sage::kQTile;
   a->scale_log2 = sm_scale * 1.4426950408889634f;
+  a->grouped = causal == 0 && (B * H) % 8 == 0;
   return SAGE_OK;
 }
 

@@ -37,6 +37,7 @@ struct AttnArgs {
   const float* v_scale;
   uint16_t* out;
   int B, H, Lq, Lkv, nqb, nkb, n_qtiles;
+  int grouped;       // 1: head-grouped tile order (not causal, B*H a multiple of 8)
   float scale_log2;  // sm_scale * log2(e)
   // Per-epoch checkpoints (trace launches only): the workgroup runs tile
   // trace_tile of head trace_bh, and wave trace_wave writes its 32 rows'

@@ -41,7 +41,9 @@ SHAPES = [(1, 1, 1, 1, 64, False), (1, 1, 1, 1, 128, True), (1, 2, 63, 63, 64, T
           (1, 1, 65, 65, 128, True), (1, 2, 127, 129, 64, False), (1, 1, 129, 127, 128, True),
           (2, 3, 200, 333, 128, True), (1, 1, 1000, 64, 64, True), (1, 1, 64, 1000, 128, True),
           (1, 1, 191, 193, 64, False), (1, 2, 300, 300, 128, True), (1, 1, 257, 1, 128, False),
-          (1, 1, 384, 384, 64, True), (1, 1, 130, 190, 128, False), (1, 1, 200, 64, 128, True)]
+          (1, 1, 384, 384, 64, True), (1, 1, 130, 190, 128, False), (1, 1, 200, 64, 128, True),
+          # non-causal with B*H a multiple of 8: the head-grouped tile order
+          (1, 8, 300, 200, 128, False), (2, 8, 129, 500, 64, False)]
 
 
 @pytest.mark.parametrize("B,H,Lq,Lkv,D,causal", SHAPES)
