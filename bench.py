@@ -236,7 +236,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=None, help="index into seeded_inputs.WORKLOADS")
     ap.add_argument("--shape", type=str, default=None,
                     help="B,H,Lq,Lkv,D,causal: a custom N(0,1) workload (K offset sigma 2) instead of a named one")
-    ap.add_argument("--kernel", choices=("auto", "fused", "split", "persistent"), default="auto",
+    ap.add_argument("--kernel", choices=("auto", "fused", "split", "persistent", "wide"), default="auto",
                     help="main-loop design timed in the main scope (sage_attn_fwd uses auto)")
     ap.add_argument("--single-samples", type=int, default=2000,
                     help="single launches timed for the main kernel's single-launch p50 (fewer under a profiler)")
@@ -292,7 +292,7 @@ def main() -> int:
             scratch.data_ptr(), n.value, sp))
 
     kernel = {"auto": _lib.SAGE_KERNEL_AUTO, "fused": _lib.SAGE_KERNEL_FUSED, "split": _lib.SAGE_KERNEL_SPLIT,
-              "persistent": _lib.SAGE_KERNEL_PERSISTENT}[args.kernel]
+              "persistent": _lib.SAGE_KERNEL_PERSISTENT, "wide": _lib.SAGE_KERNEL_WIDE}[args.kernel]
 
     def main_loop():
         _lib.check("sage_attn_fwd_prepped_kernel", L.sage_attn_fwd_prepped_kernel(

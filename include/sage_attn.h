@@ -150,12 +150,22 @@ int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t
  *                      stream for up to 64 streams per device (a further
  *                      stream runs FUSED); each launch returns its counter to
  *                      0, and calls on one stream never overlap.
+ *   SAGE_KERNEL_WIDE   the FUSED waves in 8-wave workgroups of 256 rows:
+ *                      each K/V tile copied into LDS serves twice the rows,
+ *                      and two such workgroups (four waves per SIMD) fit a
+ *                      compute unit.
  *   SAGE_KERNEL_AUTO   the design measured faster for the shape: SPLIT when
  *                      B*H*ceil(Lq/128) < 256 (fewer 128-row tiles than
  *                      compute units), FUSED otherwise. sage_attn_fwd and
  *                      sage_attn_fwd_prepped use it.
  */
-enum sage_kernel { SAGE_KERNEL_AUTO = 0, SAGE_KERNEL_FUSED = 1, SAGE_KERNEL_SPLIT = 2, SAGE_KERNEL_PERSISTENT = 3 };
+enum sage_kernel {
+    SAGE_KERNEL_AUTO = 0,
+    SAGE_KERNEL_FUSED = 1,
+    SAGE_KERNEL_SPLIT = 2,
+    SAGE_KERNEL_PERSISTENT = 3,
+    SAGE_KERNEL_WIDE = 4
+};
 
 /*
  * sage_attn_fwd_prepped with an explicit main-loop design (enum

@@ -13,11 +13,11 @@ import math
 import torch
 
 from ._lib import (LIB_PATH, SAGE_BLOCK, SAGE_KERNEL_AUTO, SAGE_KERNEL_FUSED, SAGE_KERNEL_PERSISTENT,  # noqa: F401
-                   SAGE_KERNEL_SPLIT, SageError, check, lib, status_str)
+                   SAGE_KERNEL_SPLIT, SAGE_KERNEL_WIDE, SageError, check, lib, status_str)
 
 __all__ = ["workspace_bytes", "prep_scratch_bytes", "quant_prep", "attn_fwd_prepped", "attn_fwd",
            "debug_qk_int32", "debug_codecs", "debug_epoch_trace", "SageError", "status_str", "LIB_PATH",
-           "SAGE_KERNEL_AUTO", "SAGE_KERNEL_FUSED", "SAGE_KERNEL_SPLIT", "SAGE_KERNEL_PERSISTENT"]
+           "SAGE_KERNEL_AUTO", "SAGE_KERNEL_FUSED", "SAGE_KERNEL_SPLIT", "SAGE_KERNEL_PERSISTENT", "SAGE_KERNEL_WIDE"]
 
 
 def _stream(stream=None) -> int:
@@ -84,7 +84,7 @@ def quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, stream=None) -
 def attn_fwd_prepped(prep: dict, causal: bool, sm_scale: float = None, out: torch.Tensor = None,
                      stream=None, kernel: int = SAGE_KERNEL_AUTO) -> torch.Tensor:
     """sage_attn_fwd_prepped_kernel on the dict quant_prep returns (kernel:
-    SAGE_KERNEL_AUTO, _FUSED, _SPLIT or _PERSISTENT)."""
+    SAGE_KERNEL_AUTO, _FUSED, _SPLIT, _PERSISTENT or _WIDE)."""
     B, H, Lq, Lkv, D = prep["shape"]
     if out is None:
         out = torch.empty((B, H, Lq, D), dtype=torch.bfloat16, device=prep["q_i8"].device)

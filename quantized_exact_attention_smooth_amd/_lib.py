@@ -13,7 +13,7 @@ import threading
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_attn.so")
 SAGE_BLOCK = 64
 SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ERR_HIP = 0, -1, -2, -3, -4
-SAGE_KERNEL_AUTO, SAGE_KERNEL_FUSED, SAGE_KERNEL_SPLIT, SAGE_KERNEL_PERSISTENT = 0, 1, 2, 3
+SAGE_KERNEL_AUTO, SAGE_KERNEL_FUSED, SAGE_KERNEL_SPLIT, SAGE_KERNEL_PERSISTENT, SAGE_KERNEL_WIDE = 0, 1, 2, 3, 4
 
 _lock = threading.Lock()
 _lib = None

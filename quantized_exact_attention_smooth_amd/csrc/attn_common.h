@@ -86,26 +86,36 @@ __device__ __forceinline__ uint32_t pack2_bf16(float x0, float x1) {
 // head's tiles; tile is the byte offset of the tile in it.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kRawBufferFlags = 0x00020000;  // untyped 32-bit access
-template <int D>
+// Copy instructions of one tile (64 lanes x 16 bytes each) are dealt to the
+// NW waves of the workgroup round-robin: wave w issues instructions w,
+// w + NW, ... (with fewer instructions than waves, the last waves issue none).
+template <int kInstr, int NW>
+constexpr int kInstrPerWave = (kInstr + NW - 1) / NW;
+
+template <int D, int NW = 4>
 __device__ __forceinline__ void k_tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int tile, uint8_t* lds, int w,
                                               int lane) {
-  constexpr int kPerWave = kBlock * D / 16 / 4 / 64;  // instructions per wave
+  constexpr int kInstr = kBlock * D / 16 / 64;
 #pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int p0 = (w * kPerWave + j) * 64;
+  for (int j = 0; j < kInstrPerWave<kInstr, NW>; ++j) {
+    const int i = w + NW * j;
+    if (kInstr % NW != 0 && i >= kInstr) break;  // wave-uniform
+    const int p0 = i * 64;
     const int p = p0 + lane;
     const int key = p / (D / 16), pc = p % (D / 16);
     const int c = (k_lds_off<D>(key, pc) - key * D) >> 4;  // logical chunk at physical pc
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + 16 * p0), 16, key * D + 16 * c, tile, 0, 0);
   }
 }
-template <int D>
+template <int D, int NW = 4>
 __device__ __forceinline__ void v_tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int tile, uint8_t* lds, int w,
                                               int lane) {
-  constexpr int kPerWave = D * kBlock / 16 / 4 / 64;
+  constexpr int kInstr = D * kBlock / 16 / 64;
 #pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int p0 = (w * kPerWave + j) * 64;
+  for (int j = 0; j < kInstrPerWave<kInstr, NW>; ++j) {
+    const int i = w + NW * j;
+    if (kInstr % NW != 0 && i >= kInstr) break;  // wave-uniform
+    const int p0 = i * 64;
     const int p = p0 + lane;
     const int row = p / 4, pc = p % 4;
     const int c = (v_lds_off(row, pc) - row * 64) >> 4;
@@ -114,7 +124,7 @@ __device__ __forceinline__ void v_tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int t
 }
 
 // Byte offset of 16-byte chunk `chunk` of query row `row` in an LDS Q tile
-// of 128 rows x D bytes. Rows r and r + 256/D start at the same bank, so the
+// of 32 NW rows x D bytes. Rows r and r + 256/D start at the same bank, so the
 // chunk index is XORed with row / (256/D): the 16 rows that one b128 read of
 // the QK step touches (rows q .. q + 15, one chunk each) then cover all 64
 // banks once.
@@ -127,16 +137,16 @@ __device__ __forceinline__ int q_lds_off(int row, int chunk) {
   return row * D + ((chunk ^ q_swz<D>(row)) << 4);
 }
 
-// The 128 x D Q code tile of rows q0 .. q0 + 127 of one head, copied straight
-// into LDS (direct buffer loads; wave w of 4 copies its quarter). rsrc spans
-// the head's NQB*64 code rows: rows past them read as 0.
-template <int D>
+// The (32 NW) x D Q code tile of rows q0 .. q0 + 32 NW - 1 of one head,
+// copied straight into LDS (direct buffer loads; wave w of NW copies its
+// share). rsrc spans the head's NQB*64 code rows: rows past them read as 0.
+template <int D, int NW = 4>
 __device__ __forceinline__ void q_tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int q0, uint8_t* lds, int w, int lane) {
-  constexpr int kPerWave = kQTile * D / 16 / 4 / 64;
+  constexpr int kInstr = 32 * NW * D / 16 / 64;
   constexpr int kChunksPerRow = D / 16;
 #pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int p0 = (w * kPerWave + j) * 64;
+  for (int j = 0; j < kInstrPerWave<kInstr, NW>; ++j) {
+    const int p0 = (w + NW * j) * 64;
     const int p = p0 + lane;
     const int row = p / kChunksPerRow, pc = p % kChunksPerRow;
     const int c = pc ^ q_swz<D>(row);  // logical chunk at physical pc

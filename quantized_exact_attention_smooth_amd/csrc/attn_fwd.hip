@@ -59,11 +59,12 @@ namespace sage {
 // A wave stalls on its own matrix-core steps; the other waves of the SIMD
 // issue VALU work meanwhile.
 
-// Waves per SIMD the register budget is set for: 3 at D = 128 (<= 168
-// VGPRs), 4 at D = 64 (<= 128); the trace build stores extra state and runs
-// one workgroup, so it keeps the compiler's default.
-template <int D, bool TRACE>
-constexpr int kWavesPerSimd = TRACE ? 1 : (D == 64 ? 4 : 3);
+// Waves per SIMD the register budget is set for: 3 at D = 128 with 4-wave
+// workgroups (<= 168 VGPRs; the LDS of 4 such workgroups would not fit a CU),
+// 4 at D = 64 and for 8-wave workgroups (<= 128); the trace build stores
+// extra state and runs one workgroup, so it keeps the compiler's default.
+template <int D, bool TRACE, int NW>
+constexpr int kWavesPerSimd = TRACE ? 1 : (D == 64 || NW == 8 ? 4 : 3);
 
 // The LDS of one workgroup. Four separate K/V objects (not one array) so
 // that the compiler can tell the in-flight direct fills apart from the
@@ -78,8 +79,8 @@ struct FusedLds {
   float* sv;
 };
 
-// One 128-row tile of head bh.
-template <int D, bool CAUSAL, bool TRACE>
+// One tile of 32 NW rows of head bh (NW waves of 32 rows each).
+template <int D, bool CAUSAL, bool TRACE, int NW>
 __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, const long bh, uint8_t* s_k0,
                                            uint8_t* s_k1, uint8_t* s_v0, uint8_t* s_v1, uint8_t* s_q,
                                            float* s_sv) {
@@ -93,7 +94,8 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int h = lane >> 5, ql = lane & 31;
-  const int q0 = tile * kQTile;
+  constexpr int kRows = 32 * NW;
+  const int q0 = tile * kRows;
   const int wrow0 = q0 + 32 * w;
   const int qrow = wrow0 + ql;
   const int off = a.Lkv - a.Lq;
@@ -101,7 +103,7 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
   // Epochs the workgroup stages, and the epochs this wave computes.
   int n_ep = a.nkb;
   if (CAUSAL) {
-    const int x = min(a.Lq - 1, q0 + kQTile - 1) + off;
+    const int x = min(a.Lq - 1, q0 + kRows - 1) + off;
     n_ep = x < 0 ? 0 : min(a.nkb, x / kBlock + 1);
   }
   const bool wave_on = wrow0 < a.Lq;
@@ -128,15 +130,15 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
   // The first K and V fills start before the Q codes are loaded, so that the
   // latencies overlap.
   if (n_ep > 0) {
-    k_tile_to_lds<D>(krs, 0, s_k0, w, lane);
-    v_tile_to_lds<D>(vrs, 0, s_v0, w, lane);
+    k_tile_to_lds<D, NW>(krs, 0, s_k0, w, lane);
+    v_tile_to_lds<D, NW>(vrs, 0, s_v0, w, lane);
   }
 
   // The tile's Q codes go straight into LDS with the first fills.
   const int q_bytes = a.nqb * kBlock * D;
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.q_i8 + bh * (long)q_bytes), (short)0, q_bytes, kRawBufferFlags);
-  q_tile_to_lds<D>(qrs, q0, s_q, w, lane);
+  q_tile_to_lds<D, NW>(qrs, q0, s_q, w, lane);
   int qoff[D / 32];
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) qoff[s] = q_lds_off<D>(32 * w + ql, 2 * s + h);
@@ -167,8 +169,8 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
     uint8_t* k_fill = P ? s_k0 : s_k1;  // K(e+1) replaces K(e-1)
     uint8_t* v_fill = P ? s_v0 : s_v1;  // V(e+1) replaces V(e-1)
     if (e + 1 < n_ep) {
-      k_tile_to_lds<D>(krs, (e + 1) * kBlock * D, k_fill, w, lane);
-      v_tile_to_lds<D>(vrs, (e + 1) * D * kBlock, v_fill, w, lane);
+      k_tile_to_lds<D, NW>(krs, (e + 1) * kBlock * D, k_fill, w, lane);
+      v_tile_to_lds<D, NW>(vrs, (e + 1) * D * kBlock, v_fill, w, lane);
     }
     if (e < w_ep) {
       v16i acc0, acc1;
@@ -207,33 +209,35 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
   }
 
   // Epilogue: the two halves of a query hold partial sums of l. Each wave
-  // stages its rows in one of the four K/V buffers (every wave has passed the
-  // last epoch's barrier, so none is read any more).
+  // stages its 32 rows (2D bytes each) in one of the four K/V buffers, waves
+  // 4-7 of a wide workgroup in a quarter of the Q tile (every wave has passed
+  // the last epoch's barrier, so none of them is read any more).
   const float lt = half_sum(l);
   const float rcp = (lt > 0.0f) ? 1.0f / lt : 0.0f;
   if (TRACE && w == a.trace_wave) trace_final(a, h, ql, rcp, lt);
-  uint8_t* stage = w == 0 ? s_k0 : w == 1 ? s_k1 : w == 2 ? s_v0 : s_v1;  // 32 rows x 2D bytes
+  uint8_t* stage = w == 0 ? s_k0 : w == 1 ? s_k1 : w == 2 ? s_v0 : w == 3 ? s_v1 : s_q + (w - 4) * 64 * D;
   store_rows<D>(ro, rcp, s_sv, stage, a.out, bh, a.Lq, wrow0, lane, h, ql);
 }
 
-template <int D, bool CAUSAL, bool TRACE, bool PERSIST>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, TRACE>)))
+template <int D, bool CAUSAL, bool TRACE, bool PERSIST, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, TRACE, NW>)))
 void attn_fwd_kernel(AttnArgs a) {
+  static_assert(NW == 4 || NW == 8, "4- or 8-wave workgroups");
   __shared__ __attribute__((aligned(16))) uint8_t s_k0[kBlock * D];
   __shared__ __attribute__((aligned(16))) uint8_t s_k1[kBlock * D];
   __shared__ __attribute__((aligned(16))) uint8_t s_v0[D * kBlock];
   __shared__ __attribute__((aligned(16))) uint8_t s_v1[D * kBlock];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[kQTile * D];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[32 * NW * D];
   __shared__ __attribute__((aligned(16))) float s_sv[D];
   if (TRACE) {
-    fused_tile<D, CAUSAL, TRACE>(a, a.trace_tile, a.trace_bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    fused_tile<D, CAUSAL, TRACE, NW>(a, a.trace_tile, a.trace_bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
     return;
   }
   if (!PERSIST) {
     int tile;
     long bh;
     work_item(a, blockIdx.x, tile, bh);
-    fused_tile<D, CAUSAL, TRACE>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    fused_tile<D, CAUSAL, TRACE, NW>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
     return;
   }
   // Persistent workgroups take work items from counters (fetch-and-add), one
@@ -263,7 +267,7 @@ void attn_fwd_kernel(AttnArgs a) {
     int tile;
     long bh;
     work_item(a, x + kXcds * k, tile, bh);
-    fused_tile<D, CAUSAL, TRACE>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    fused_tile<D, CAUSAL, TRACE, NW>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
     // Every wave is done with the LDS (the epilogue staged its rows in the
     // K/V buffers) and with s_item before the next item refills them.
     __syncthreads();
@@ -331,35 +335,42 @@ __global__ __launch_bounds__(256) void codecs_debug_kernel(const float* __restri
 
 // ------------------------------------------------------------ launchers
 
-template <int D, bool C, bool T, bool P>
+template <int D, bool C, bool T, bool P, int NW>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   const long blocks = T ? 1L : P ? (long)a.persist_grid : (long)a.n_qtiles * a.B * a.H;
-  attn_fwd_kernel<D, C, T, P><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(a);
+  attn_fwd_kernel<D, C, T, P, NW><<<dim3((unsigned)blocks), 64 * NW, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <bool T, bool P>
+template <bool T, bool P, int NW>
 static hipError_t launch_attn_v(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
   if (D == 128)
-    return causal ? launch_attn_t<128, true, T, P>(a, stream) : launch_attn_t<128, false, T, P>(a, stream);
-  return causal ? launch_attn_t<64, true, T, P>(a, stream) : launch_attn_t<64, false, T, P>(a, stream);
+    return causal ? launch_attn_t<128, true, T, P, NW>(a, stream) : launch_attn_t<128, false, T, P, NW>(a, stream);
+  return causal ? launch_attn_t<64, true, T, P, NW>(a, stream) : launch_attn_t<64, false, T, P, NW>(a, stream);
 }
 
 hipError_t launch_attn_fused(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream) {
-  return trace ? launch_attn_v<true, false>(a, D, causal, stream) : launch_attn_v<false, false>(a, D, causal, stream);
+  return trace ? launch_attn_v<true, false, 4>(a, D, causal, stream)
+               : launch_attn_v<false, false, 4>(a, D, causal, stream);
+}
+hipError_t launch_attn_wide(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream) {
+  return trace ? launch_attn_v<true, false, 8>(a, D, causal, stream)
+               : launch_attn_v<false, false, 8>(a, D, causal, stream);
 }
 hipError_t launch_attn_persistent(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  return launch_attn_v<false, true>(a, D, causal, stream);
+  return launch_attn_v<false, true, 4>(a, D, causal, stream);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream) {
   if (kernel == kKernelSplit) return launch_attn_split(a, D, causal, false, stream);
   if (kernel == kKernelPersistent) return launch_attn_persistent(a, D, causal, stream);
+  if (kernel == kKernelWide) return launch_attn_wide(a, D, causal, false, stream);
   return launch_attn_fused(a, D, causal, false, stream);
 }
 hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream) {
-  return kernel == kKernelSplit ? launch_attn_split(a, D, causal, true, stream)
-                                : launch_attn_fused(a, D, causal, true, stream);
+  if (kernel == kKernelSplit) return launch_attn_split(a, D, causal, true, stream);
+  if (kernel == kKernelWide) return launch_attn_wide(a, D, causal, true, stream);
+  return launch_attn_fused(a, D, causal, true, stream);
 }
 
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream) {

@@ -163,6 +163,7 @@ int resolve_kernel(int kernel, int B, int H, int Lq) {
   if (kernel == SAGE_KERNEL_FUSED) return sage::kKernelFused;
   if (kernel == SAGE_KERNEL_SPLIT) return sage::kKernelSplit;
   if (kernel == SAGE_KERNEL_PERSISTENT) return sage::kKernelPersistent;
+  if (kernel == SAGE_KERNEL_WIDE) return sage::kKernelWide;
   return -1;
 }
 
@@ -268,6 +269,12 @@ int sage_quant_prep(const void* q, const void* k, const void* v, int B, int H, i
                     scratch_bytes, stream);
 }
 
+// Tiles per head for the design's tile height.
+void set_tiles(sage::AttnArgs* a, int kind) {
+  const int rows = sage::tile_rows(kind);
+  a->n_qtiles = (a->Lq + rows - 1) / rows;
+}
+
 // Counter and grid of a persistent launch: one workgroup per resident slot
 // (three per compute unit at D = 128, four at D = 64), at most one per work
 // item. Falls back to the non-persistent design (*kind) when no counter is
@@ -309,6 +316,7 @@ int sage_attn_fwd_prepped_kernel(const int8_t* q_i8, const float* q_scale, const
   if (st != SAGE_OK) return st;
   int kind = resolve_kernel(kernel, B, H, Lq);
   if (kind < 0) return SAGE_ERR_INVALID_ARG;
+  set_tiles(&a, kind);
   if (kind == sage::kKernelPersistent && !persistent_setup(&a, D, stream, &kind)) return SAGE_ERR_HIP;
   return hip_status(sage::launch_attn(a, D, causal == 1, kind, (hipStream_t)stream));
 }
@@ -328,15 +336,17 @@ int sage_debug_epoch_trace(const int8_t* q_i8, const float* q_scale, const int8_
   const int st = attn_args(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, out, B, H, Lq, Lkv, D, causal,
                            sm_scale, &a);
   if (st != SAGE_OK) return st;
-  const int kind = resolve_kernel(kernel, B, H, Lq);
+  int kind = resolve_kernel(kernel, B, H, Lq);
   if (kind < 0) return SAGE_ERR_INVALID_ARG;
+  if (kind == sage::kKernelPersistent) kind = sage::kKernelFused;  // the same tile code, traced on one tile
+  set_tiles(&a, kind);
   if (b < 0 || b >= B || h < 0 || h >= H || row0 < 0 || row0 >= Lq || row0 % 32 != 0) return SAGE_ERR_INVALID_ARG;
   if (!stats || !p8 || !pv || !ro || misaligned(stats, 16) || misaligned(p8, 4) || misaligned(pv, 4) ||
       misaligned(ro, 4))
     return SAGE_ERR_INVALID_ARG;
   a.trace_bh = b * H + h;
-  a.trace_tile = row0 / sage::kQTile;
-  a.trace_wave = (row0 % sage::kQTile) / 32;
+  a.trace_tile = row0 / sage::tile_rows(kind);
+  a.trace_wave = (row0 % sage::tile_rows(kind)) / 32;
   a.tr_stats = stats;
   a.tr_p8 = p8;
   a.tr_pv = pv;
@@ -367,7 +377,9 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
                 (const float*)(ws + l.k_scale), (const uint8_t*)(ws + l.v_fp8), (const float*)(ws + l.v_scale),
                 out, B, H, Lq, Lkv, D, causal, sm_scale, &a);
   if (s != SAGE_OK) return s;
-  return hip_status(sage::launch_attn(a, D, causal == 1, auto_kernel(B, H, Lq), (hipStream_t)stream));
+  const int kind = auto_kernel(B, H, Lq);
+  set_tiles(&a, kind);
+  return hip_status(sage::launch_attn(a, D, causal == 1, kind, (hipStream_t)stream));
 }
 
 int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int Lq, int Lkv, int D,

@@ -66,6 +66,10 @@ struct QkDebugArgs {
 constexpr int kKernelFused = 1;  // every wave runs QK, softmax and PV for its rows
 constexpr int kKernelSplit = 2;  // softmax waves and PV waves own separate state
 constexpr int kKernelPersistent = 3;  // fused waves in persistent workgroups fed by a work counter
+constexpr int kKernelWide = 4;        // fused waves in 8-wave (256-row) workgroups
+
+// Query rows per workgroup of a main-loop design.
+constexpr int tile_rows(int kernel) { return kernel == kKernelWide ? 256 : kQTile; }
 
 int prep_n_split(int Lkv);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
@@ -73,6 +77,7 @@ hipError_t launch_attn(const AttnArgs& a, int D, bool causal, int kernel, hipStr
 hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream);
 hipError_t launch_attn_fused(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream);
 hipError_t launch_attn_split(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream);
+hipError_t launch_attn_wide(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream);
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream);
 hipError_t launch_codecs_debug(const float* x, int n, uint8_t* p8, uint16_t* bf16, hipStream_t stream);
 

@@ -123,7 +123,7 @@ def test_prep_and_prepped_reject_bad_arguments(lib):
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 0, 0.0, None) == -2
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 3, 0.0, None) == -1
     k = lib.sage_attn_fwd_prepped_kernel
-    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, 4, None) == -1   # unknown design
+    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, 5, None) == -1   # unknown design
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, -1, None) == -1
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 64, 0, 0.0, 2, None) == -1
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 0, 0.0, 1, None) == -2

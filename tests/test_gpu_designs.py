@@ -21,7 +21,7 @@ from _parity import assert_out_close, oracle_preps, oracle_rows, say
 pytestmark = pytest.mark.gpu
 
 FUSED = sage.SAGE_KERNEL_FUSED
-DESIGNS = {"split": sage.SAGE_KERNEL_SPLIT, "persistent": sage.SAGE_KERNEL_PERSISTENT}
+DESIGNS = {"split": sage.SAGE_KERNEL_SPLIT, "persistent": sage.SAGE_KERNEL_PERSISTENT, "wide": sage.SAGE_KERNEL_WIDE}
 
 
 @pytest.fixture(params=sorted(DESIGNS))

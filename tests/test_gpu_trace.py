@@ -49,7 +49,7 @@ CASES = {
 }
 
 
-KERNELS = {"fused": sage.SAGE_KERNEL_FUSED, "split": sage.SAGE_KERNEL_SPLIT}
+KERNELS = {"fused": sage.SAGE_KERNEL_FUSED, "split": sage.SAGE_KERNEL_SPLIT, "wide": sage.SAGE_KERNEL_WIDE}
 
 
 @pytest.mark.parametrize("kernel", sorted(KERNELS))
