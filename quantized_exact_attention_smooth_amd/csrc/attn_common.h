@@ -254,6 +254,40 @@ __device__ __forceinline__ int p4(const int (&x)[32], int d, float c, float m_us
 struct NoHook {
   __device__ __forceinline__ void operator()(int) const {}
 };
+
+// Large scores. The direct exponent fma(S, c, -m) carries the rounding error
+// of the running max m = RN(Smax c) (up to half an ulp of m) into every key
+// of the epoch. Within an epoch that factor multiplies P and l alike, and
+// while |m| < 2^12 it is below 2^-13 of an exponent unit; but at very large
+// scores it would push the top key's p far above 1, past the E4M3 range.
+// When some row of the wave has |m| >= 2^12 (wave-uniform test, one compare
+// per epoch), the epoch takes its scores relative to the row's integer max
+// instead: p = exp2((S - Smax) c - (m - m_e)), with S - Smax exact (|S| <
+// 2^22) and m - m_e >= 0 (m_e = RN(Smax c), the epoch's own max), so every
+// exponent is <= 0 and the top key of the epoch that set m gets p = 1.
+constexpr float kRebaseLog2 = 4096.0f;
+__device__ __forceinline__ bool large_scores(float m_use) {
+  return __builtin_amdgcn_ballot_w64(__builtin_fabsf(m_use) >= kRebaseLog2) != 0;
+}
+
+// p4 in the large-score form: x[t] - mx is taken in unsigned arithmetic (for
+// a lane that sees no key of the epoch mx is INT_MIN and the difference
+// wraps; such keys are hidden, p = 0), dm = m - m_e (+inf for such a lane).
+template <bool MASKED>
+__device__ __forceinline__ int p4_rebased(const int (&x)[32], int d, int mx, float c, float dm, int dlim,
+                                          float& ps) {
+  float p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = 4 * d + j;
+    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)(int)((unsigned)x[t] - (unsigned)mx), c, -dm));
+    p[j] = (MASKED && t > dlim) ? 0.0f : e;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ps = (d == 0 && j == 0) ? p[0] : ps + p[j];
+  return pack4_fp8(p[0], p[1], p[2], p[3]);
+}
+
 template <typename Hook = NoHook>
 __device__ __forceinline__ void softmax_epoch(const v16i& acc0, const v16i& acc1, float c, bool masked,
                                               int dlim, bool sees, float& m, float& l, v8i& pb, float& alpha,
@@ -275,10 +309,18 @@ __device__ __forceinline__ void softmax_epoch(const v16i& acc0, const v16i& acc1
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     alpha = __builtin_amdgcn_exp2f(m - m_use);
     moved = __builtin_amdgcn_ballot_w64(up) != 0;
+    if (large_scores(m_use)) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      pb[d] = p4<true>(x, d, c, m_use, dlim, ps);
-      if (d == 3) hook(0);
+      for (int d = 0; d < 8; ++d) {
+        pb[d] = p4_rebased<true>(x, d, mx, c, m_use - mt, dlim, ps);
+        if (d == 3) hook(0);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        pb[d] = p4<true>(x, d, c, m_use, dlim, ps);
+        if (d == 3) hook(0);
+      }
     }
     m = m_new;
   } else {
@@ -288,10 +330,18 @@ __device__ __forceinline__ void softmax_epoch(const v16i& acc0, const v16i& acc1
     const float m_new = up ? mt : m;
     alpha = __builtin_amdgcn_exp2f(m - m_new);
     moved = __builtin_amdgcn_ballot_w64(up) != 0;
+    if (large_scores(m_new)) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      pb[d] = p4<false>(x, d, c, m_new, dlim, ps);
-      if (d == 3) hook(0);
+      for (int d = 0; d < 8; ++d) {
+        pb[d] = p4_rebased<false>(x, d, mx, c, m_new - mt, dlim, ps);
+        if (d == 3) hook(0);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        pb[d] = p4<false>(x, d, c, m_new, dlim, ps);
+        if (d == 3) hook(0);
+      }
     }
     m = m_new;
   }

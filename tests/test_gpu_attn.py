@@ -268,6 +268,28 @@ def test_power_of_two_scalings_act_exactly(causal, gpu_device):
     np.testing.assert_array_equal(got_q, out)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_scores_stay_finite_and_match_the_oracle(causal, gpu_device):
+    """Rows whose running max reaches 2^12 in the log2 domain take their
+    exponents relative to the row's integer top score. Head 1 has Q times
+    3000 (row maxima 1e4 to 2.3e4 log2 units, where the oracle's own fp32
+    score rounding stays near 2^-9 of a unit) and must meet the output bar;
+    head 2 has Q times 1e30 (scores near 1e31, where fp32 arithmetic leaves
+    only the top keys with p > 0) and must give the oracle's values too.
+    Every output is finite."""
+    B, H, L, D = 1, 3, 333, 128
+    q, k, v = si.make_qkv(B, H, L, L, D, "normal", 2.0, seed=91)
+    q = q.clone()
+    q[:, 1] *= 3000.0
+    q[:, 2] *= 1e30
+    sc = 1 / math.sqrt(D)
+    say(f"attn parity: large scores, causal={causal}")
+    out = _gpu_out(q, k, v, causal, sc, gpu_device)
+    assert np.all(np.isfinite(oracle.bf16_to_f32(out)))
+    for (b, h), o in oracle_preps(q, k, v, [(0, 0), (0, 1), (0, 2)]).items():
+        assert_out_close(out[b, h], oracle_rows(o, causal, sc, 0, L), f"attn: large scores head {h}")
+
+
 def test_concurrent_calls_on_two_streams_match_sequential(gpu_device):
     """Calls keep no state between them: two host threads, each on its own
     stream (default priority), run different shapes at the same time, and

@@ -76,6 +76,28 @@ def test_prep_degenerate_blocks(gpu_device):
     assert g["v_scale"][0, 0, 3] == 0 and np.all(g["v8"][0, 0, :, 3] == 0)
 
 
+def test_prep_tiny_and_subnormal_scales(gpu_device):
+    """Blocks and channels whose scale is below 2^-60, where the quotients
+    are taken by division rather than from the reciprocal, and subnormal bf16
+    inputs (scales that are fp32 subnormals): codes and scales bit-exact
+    against the oracle's IEEE single divisions."""
+    B, H, L, D = 1, 2, 260, 128
+    q, k, v = si.make_qkv(B, H, L, L, D, "normal", 1.0, seed=6)
+    q, k, v = q.clone(), k.clone(), v.clone()
+    q[:, 0, :64] *= 1e-30
+    q[:, 0, 64:128] *= 1e-39
+    q[:, 1, 192:] *= 1e-25
+    k[:, 0] *= 1e-30           # every K block of head 0 after smoothing
+    k[:, 1, :, :40] *= 1e-39   # subnormal channels of head 1
+    v[:, 0, :, 5] *= 1e-30     # one V channel below the fast path
+    v[:, 1, :, :16] *= 1e-39
+    say("prep parity: tiny and subnormal scales")
+    g = _run(q, k, v, gpu_device)
+    for (b, h), o in oracle_preps(q, k, v, [(0, 0), (0, 1)]).items():
+        assert_prep_equal(g, o, b, h)
+    assert 0 < g["q_scale"][0, 0, 1] < 2.0 ** -126  # a subnormal scale was produced and kept
+
+
 def test_prep_is_deterministic(gpu_device):
     w = si.WORKLOADS[1]
     q, k, v = (t.to(gpu_device) for t in si.workload_qkv(w))
