@@ -69,16 +69,17 @@ def _src_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _profile(workload: str) -> dict:
+def _profile(workload: str, design: str) -> dict:
     """The committed counter summary of the main kernel on this workload
     (HBM bytes per launch, matrix-core and VALU busy fractions), only if it
-    was taken on the current kernel sources; {} otherwise."""
+    was taken on the current kernel sources and for the design timed (the
+    summaries are taken with the automatic choice); {} otherwise."""
     p = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm.json")
     if not os.path.exists(p):
         return {}
     with open(p) as f:
         d = json.load(f)
-    return d if d.get("src_hash") == _src_hash() else {}
+    return d if d.get("src_hash") == _src_hash() and d.get("design", "auto") == design else {}
 
 
 def cpu_model() -> str:
@@ -236,8 +237,10 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=None, help="index into seeded_inputs.WORKLOADS")
     ap.add_argument("--shape", type=str, default=None,
                     help="B,H,Lq,Lkv,D,causal: a custom N(0,1) workload (K offset sigma 2) instead of a named one")
-    ap.add_argument("--kernel", choices=("auto", "fused", "split", "persistent", "wide"), default="auto",
-                    help="main-loop design timed in the main scope (sage_attn_fwd uses auto)")
+    ap.add_argument("--kernel", choices=("auto", "fused", "split", "persistent", "wide", "entry"), default="auto",
+                    help="main-loop design timed in the main scope (sage_attn_fwd uses auto); entry, which "
+                         "codes Q inside the main kernel, exists for the whole path only: it replaces both the "
+                         "main and the end-to-end scope")
     ap.add_argument("--single-samples", type=int, default=2000,
                     help="single launches timed for the main kernel's single-launch p50 (fewer under a profiler)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -292,7 +295,9 @@ def main() -> int:
             scratch.data_ptr(), n.value, sp))
 
     kernel = {"auto": _lib.SAGE_KERNEL_AUTO, "fused": _lib.SAGE_KERNEL_FUSED, "split": _lib.SAGE_KERNEL_SPLIT,
-              "persistent": _lib.SAGE_KERNEL_PERSISTENT, "wide": _lib.SAGE_KERNEL_WIDE}[args.kernel]
+              "persistent": _lib.SAGE_KERNEL_PERSISTENT, "wide": _lib.SAGE_KERNEL_WIDE,
+              "entry": _lib.SAGE_KERNEL_ENTRY}[args.kernel]
+    entry = kernel == _lib.SAGE_KERNEL_ENTRY
 
     def main_loop():
         _lib.check("sage_attn_fwd_prepped_kernel", L.sage_attn_fwd_prepped_kernel(
@@ -306,9 +311,17 @@ def main() -> int:
     out_e2e = torch.empty_like(out)
 
     def e2e():
+        if entry:
+            _lib.check("sage_attn_fwd_kernel", L.sage_attn_fwd_kernel(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), out_e2e.data_ptr(), B, H, Lq, Lkv, D, causal,
+                w.sm_scale, kernel, ws.data_ptr(), nws.value, sp))
+            return
         _lib.check("sage_attn_fwd", L.sage_attn_fwd(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out_e2e.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale,
             ws.data_ptr(), nws.value, sp))
+
+    if entry:  # the entry design's main kernel runs only inside the whole path
+        main_loop = e2e
 
     for _ in range(args.warmup):
         e2e()
@@ -372,7 +385,7 @@ def main() -> int:
     ms_step = wall * 1e3 / K
     ops = w.metric_ops
     achieved = ops / (main_avg * 1e-3) / 1e12
-    prof = _profile(w.name)
+    prof = _profile(w.name, args.kernel)
     traffic = prof.get("bytes_per_launch")
     prep_bytes = B * H * (Lq + 2 * Lkv) * D * 2 + B * H * (nqb + 2 * nkb) * 64 * D
 
@@ -384,7 +397,9 @@ def main() -> int:
                    "k_offset_sigma": w.k_offset_sigma, "dist": w.dist, "main_kernel": args.kernel},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TOPS",
                      "frac": achieved / PEAK_TOPS, "traffic": traffic,
-                     "scope": "main kernel (sage_attn_fwd_prepped); value is the whole step",
+                     "scope": ("whole path of the entry design (sage_attn_fwd_kernel: the Q step runs inside "
+                               "the main kernel); value is the whole step") if entry else
+                              "main kernel (sage_attn_fwd_prepped); value is the whole step",
                      "e2e_frac": ops / (e2e_avg * 1e-3) / 1e12 / PEAK_TOPS,
                      "hbm_GBps": traffic / (main_avg * 1e-3) / 1e9 if traffic else None,
                      "mfma_busy": prof.get("mfma_busy"), "valu_busy": prof.get("valu_busy"),

@@ -154,6 +154,17 @@ int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t
  *                      each K/V tile copied into LDS serves twice the rows,
  *                      and two such workgroups (four waves per SIMD) fit a
  *                      compute unit.
+ *   SAGE_KERNEL_ENTRY  (sage_attn_fwd_kernel only) the FUSED waves with the
+ *                      Q INT8 step moved into the main loop (Experiment Log,
+ *                      "Closed Prior Work": the P1 entry fusion, reused
+ *                      inside the attention pipeline): the preparation pass
+ *                      codes K and V only, and each workgroup reads its 128
+ *                      rows of bf16 Q and codes them straight into its LDS Q
+ *                      tile with the preparation pass's arithmetic (the same
+ *                      codes and scales), so Q codes never pass through
+ *                      memory; the workspace's Q code and Q scale areas are
+ *                      left unwritten. Calls on prepared operands return
+ *                      SAGE_ERR_INVALID_ARG for it.
  *   SAGE_KERNEL_AUTO   the design measured faster for the shape: SPLIT when
  *                      B*H*ceil(Lq/128) < 256 (fewer 128-row tiles than
  *                      compute units), FUSED otherwise. sage_attn_fwd and
@@ -164,12 +175,14 @@ enum sage_kernel {
     SAGE_KERNEL_FUSED = 1,
     SAGE_KERNEL_SPLIT = 2,
     SAGE_KERNEL_PERSISTENT = 3,
-    SAGE_KERNEL_WIDE = 4
+    SAGE_KERNEL_WIDE = 4,
+    SAGE_KERNEL_ENTRY = 5
 };
 
 /*
  * sage_attn_fwd_prepped with an explicit main-loop design (enum
- * sage_kernel); any other value returns SAGE_ERR_INVALID_ARG.
+ * sage_kernel, other than SAGE_KERNEL_ENTRY); any other value returns
+ * SAGE_ERR_INVALID_ARG.
  */
 int sage_attn_fwd_prepped_kernel(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                  const float* k_scale, const uint8_t* v_fp8, const float* v_scale, void* out,
@@ -187,6 +200,15 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
                   void* stream);
 
 /*
+ * sage_attn_fwd with an explicit main-loop design (enum sage_kernel,
+ * SAGE_KERNEL_ENTRY included); any other value returns SAGE_ERR_INVALID_ARG.
+ * Every argument is checked before anything is launched.
+ */
+int sage_attn_fwd_kernel(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
+                         int D, int causal, float sm_scale, int kernel, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * Debug: the exact int32 QK accumulators of chosen 64x64 tiles, computed by
  * the same LDS staging and INT8 matrix-core code as the main loop
  * (Experiment Log, "Phase 2B": the "QK" checkpoint).
@@ -201,8 +223,9 @@ int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, in
  * Debug: per-epoch checkpoints of 32 query rows (Experiment Log, "Phase 2B
  * Fixed Aligned Numerical Prototype": the QK, m, d, FP8 probability,
  * rescale, PV, FP32 RO and reciprocal checkpoints). Runs the main loop of
- * design `kernel` (enum sage_kernel) on the one 128-row tile of head (b, h)
- * that holds rows row0 .. row0 + 31 (row0 a multiple of 32, < Lq); the waves
+ * design `kernel` (enum sage_kernel, not SAGE_KERNEL_ENTRY) on the one tile
+ * of head (b, h) that holds rows row0 .. row0 + 31 (row0 a multiple of 32,
+ * < Lq); the waves
  * owning those rows write, for row t = row0 + i and every epoch e they
  * compute (e below the rows' epoch count; the caller pre-fills the buffers
  * to recognise the rest):

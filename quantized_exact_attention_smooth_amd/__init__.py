@@ -12,12 +12,14 @@ import math
 
 import torch
 
-from ._lib import (LIB_PATH, SAGE_BLOCK, SAGE_KERNEL_AUTO, SAGE_KERNEL_FUSED, SAGE_KERNEL_PERSISTENT,  # noqa: F401
-                   SAGE_KERNEL_SPLIT, SAGE_KERNEL_WIDE, SageError, check, lib, status_str)
+from ._lib import (LIB_PATH, SAGE_BLOCK, SAGE_KERNEL_AUTO, SAGE_KERNEL_ENTRY, SAGE_KERNEL_FUSED,  # noqa: F401
+                   SAGE_KERNEL_PERSISTENT, SAGE_KERNEL_SPLIT, SAGE_KERNEL_WIDE, SageError, check, lib,
+                   status_str)
 
 __all__ = ["workspace_bytes", "prep_scratch_bytes", "quant_prep", "attn_fwd_prepped", "attn_fwd",
            "debug_qk_int32", "debug_codecs", "debug_epoch_trace", "SageError", "status_str", "LIB_PATH",
-           "SAGE_KERNEL_AUTO", "SAGE_KERNEL_FUSED", "SAGE_KERNEL_SPLIT", "SAGE_KERNEL_PERSISTENT", "SAGE_KERNEL_WIDE"]
+           "SAGE_KERNEL_AUTO", "SAGE_KERNEL_FUSED", "SAGE_KERNEL_SPLIT", "SAGE_KERNEL_PERSISTENT", "SAGE_KERNEL_WIDE",
+           "SAGE_KERNEL_ENTRY"]
 
 
 def _stream(stream=None) -> int:
@@ -84,7 +86,8 @@ def quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, stream=None) -
 def attn_fwd_prepped(prep: dict, causal: bool, sm_scale: float = None, out: torch.Tensor = None,
                      stream=None, kernel: int = SAGE_KERNEL_AUTO) -> torch.Tensor:
     """sage_attn_fwd_prepped_kernel on the dict quant_prep returns (kernel:
-    SAGE_KERNEL_AUTO, _FUSED, _SPLIT, _PERSISTENT or _WIDE)."""
+    SAGE_KERNEL_AUTO, _FUSED, _SPLIT, _PERSISTENT or _WIDE; _ENTRY needs bf16
+    Q and is refused)."""
     B, H, Lq, Lkv, D = prep["shape"]
     if out is None:
         out = torch.empty((B, H, Lq, D), dtype=torch.bfloat16, device=prep["q_i8"].device)
@@ -99,9 +102,11 @@ def attn_fwd_prepped(prep: dict, causal: bool, sm_scale: float = None, out: torc
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, sm_scale: float = None,
-             out: torch.Tensor = None, workspace: torch.Tensor = None, stream=None) -> torch.Tensor:
-    """sage_attn_fwd: preparation and main loop. workspace (uint8, optional)
-    is reused when large enough."""
+             out: torch.Tensor = None, workspace: torch.Tensor = None, stream=None,
+             kernel: int = SAGE_KERNEL_AUTO) -> torch.Tensor:
+    """sage_attn_fwd (kernel SAGE_KERNEL_AUTO) or sage_attn_fwd_kernel (any
+    other design, SAGE_KERNEL_ENTRY included): preparation and main loop.
+    workspace (uint8, optional) is reused when large enough."""
     B, H, Lq, Lkv, D = _dims(q, k)
     if tuple(v.shape) != tuple(k.shape):
         raise ValueError("v must match k")
@@ -110,11 +115,14 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, sm
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, H, Lq, D), dtype=torch.bfloat16, device=q.device)
-    st = lib().sage_attn_fwd(_dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"),
-                             _dev(v, torch.bfloat16, "v"), _dev(out, torch.bfloat16, "out"), B, H, Lq,
-                             Lkv, D, int(bool(causal)), float(sm_scale) if sm_scale else 0.0,
-                             _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
-    check("sage_attn_fwd", st)
+    args = (_dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+            _dev(out, torch.bfloat16, "out"), B, H, Lq, Lkv, D, int(bool(causal)),
+            float(sm_scale) if sm_scale else 0.0)
+    ws = (_dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    if kernel == SAGE_KERNEL_AUTO:
+        check("sage_attn_fwd", lib().sage_attn_fwd(*args, *ws))
+    else:
+        check("sage_attn_fwd_kernel", lib().sage_attn_fwd_kernel(*args, int(kernel), *ws))
     return out
 
 

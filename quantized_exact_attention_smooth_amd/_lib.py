@@ -13,7 +13,8 @@ import threading
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage_attn.so")
 SAGE_BLOCK = 64
 SAGE_OK, SAGE_ERR_INVALID_ARG, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ERR_HIP = 0, -1, -2, -3, -4
-SAGE_KERNEL_AUTO, SAGE_KERNEL_FUSED, SAGE_KERNEL_SPLIT, SAGE_KERNEL_PERSISTENT, SAGE_KERNEL_WIDE = 0, 1, 2, 3, 4
+(SAGE_KERNEL_AUTO, SAGE_KERNEL_FUSED, SAGE_KERNEL_SPLIT, SAGE_KERNEL_PERSISTENT, SAGE_KERNEL_WIDE,
+ SAGE_KERNEL_ENTRY) = 0, 1, 2, 3, 4, 5
 
 _lock = threading.Lock()
 _lib = None
@@ -51,6 +52,8 @@ def lib() -> ctypes.CDLL:
             L.sage_attn_fwd_prepped_kernel.restype = I
             L.sage_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, F, P, Z, P]
             L.sage_attn_fwd.restype = I
+            L.sage_attn_fwd_kernel.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
+            L.sage_attn_fwd_kernel.restype = I
             L.sage_debug_qk_int32.argtypes = [P, P, I, I, I, I, I, P, I, P, P]
             L.sage_debug_qk_int32.restype = I
             L.sage_debug_codecs.argtypes = [P, I, P, P, P]

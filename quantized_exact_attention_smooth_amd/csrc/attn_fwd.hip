@@ -79,11 +79,77 @@ struct FusedLds {
   float* sv;
 };
 
-// One tile of 32 NW rows of head bh (NW waves of 32 rows each).
-template <int D, bool CAUSAL, bool TRACE, int NW>
+// Entry design: the Q codes of a tile, made by the main loop from the bf16
+// rows exactly as the preparation pass makes them (an INT8 scale per 64-row
+// block: s = absmax / 127 over the block's rows < Lq; code = clamp(rint(x /
+// s), +-127) with the quotient rounded as an IEEE division; rows >= Lq code
+// 0), so the codes and scales are the same bits. Each wave codes its own 32
+// rows (wrow0 ..) into the LDS Q tile; the two waves of a 64-row block
+// exchange their absmax through s_qmax (one slot per wave). Every wave of
+// the workgroup calls it (it holds a barrier). Returns the block's s.
+template <int D, int NW>
+__device__ __forceinline__ float q_code_tile(const uint16_t* __restrict__ qh, int Lq, int wrow0, uint8_t* s_q,
+                                             float* s_qmax, int w, int lane) {
+  constexpr int kChunks = D / 16;               // 16-code chunks per row
+  constexpr int kPerLane = 32 * kChunks / 64;   // chunks per lane: 4 at D = 128, 2 at D = 64
+  uint4 raw[kPerLane][2];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    const int p = lane + 64 * j, row = wrow0 + p / kChunks, c = p % kChunks;
+    if (row < Lq) {
+      const uint4* src = reinterpret_cast<const uint4*>(qh + (long)row * D + 16 * c);
+      raw[j][0] = src[0];
+      raw[j][1] = src[1];
+    } else {
+      raw[j][0] = raw[j][1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  float amax = 0.0f;  // rows >= Lq hold zeros, which leave the absmax as it is
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float f[8];
+      unpack8(raw[j][hf], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (lane == 0) s_qmax[w] = amax;
+  __syncthreads();
+  const float am = fmaxf(s_qmax[w], s_qmax[w ^ 1]);
+  const float s = am / 127.0f;
+  const bool fast = s >= kFastDivMinScale;  // uniform over the block
+  const float r = fast ? 1.0f / s : 0.0f;
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};
+    if (am != 0.0f) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float f[8];
+        unpack8(raw[j][hf], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = fast ? div_rn(f[i], s, r) : f[i] / s;
+          cw[2 * hf + (i >> 2)] |= code_i8(x) << (8 * (i & 3));
+        }
+      }
+    }
+    const int p = lane + 64 * j;
+    *reinterpret_cast<uint4*>(s_q + q_lds_off<D>(32 * w + p / kChunks, p % kChunks)) =
+        make_uint4(cw[0], cw[1], cw[2], cw[3]);
+  }
+  return s;
+}
+
+// One tile of 32 NW rows of head bh (NW waves of 32 rows each). ENTRY: the
+// tile's Q codes are made here from bf16 Q (q_code_tile) instead of copied.
+template <int D, bool CAUSAL, bool TRACE, int NW, bool ENTRY>
 __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, const long bh, uint8_t* s_k0,
                                            uint8_t* s_k1, uint8_t* s_v0, uint8_t* s_v1, uint8_t* s_q,
-                                           float* s_sv) {
+                                           float* s_sv, float* s_qmax) {
   // The thread index is made opaque here, so that the per-lane offsets
   // derived from it are computed where they are used, in every tile, rather
   // than hoisted out of a persistent workgroup's tile loop (where they would
@@ -134,17 +200,24 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
     v_tile_to_lds<D, NW>(vrs, 0, s_v0, w, lane);
   }
 
-  // The tile's Q codes go straight into LDS with the first fills.
-  const int q_bytes = a.nqb * kBlock * D;
-  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.q_i8 + bh * (long)q_bytes), (short)0, q_bytes, kRawBufferFlags);
-  q_tile_to_lds<D, NW>(qrs, q0, s_q, w, lane);
+  if (tid < D) s_sv[tid] = a.v_scale[bh * D + tid];
+  // The tile's Q codes go straight into LDS with the first fills (or are
+  // made there from bf16 Q).
+  float sq;
+  if (ENTRY) {
+    const float s = q_code_tile<D, NW>(a.q + bh * (long)a.Lq * D, a.Lq, wrow0, s_q, s_qmax, w, lane);
+    sq = wave_on ? s : 0.0f;
+  } else {
+    const int q_bytes = a.nqb * kBlock * D;
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.q_i8 + bh * (long)q_bytes), (short)0, q_bytes, kRawBufferFlags);
+    q_tile_to_lds<D, NW>(qrs, q0, s_q, w, lane);
+    sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
+  }
   int qoff[D / 32];
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) qoff[s] = q_lds_off<D>(32 * w + ql, 2 * s + h);
-  const float sq = wave_on ? a.q_scale[bh * a.nqb + wrow0 / kBlock] : 0.0f;
   const float cq = sq * a.scale_log2;
-  if (tid < D) s_sv[tid] = a.v_scale[bh * D + tid];
 
   // The QK read offsets are computed once; the empty asm keeps the compiler
   // from rebuilding them from their parts in every epoch (four VALU adds).
@@ -219,7 +292,7 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
   store_rows<D>(ro, rcp, s_sv, stage, a.out, bh, a.Lq, wrow0, lane, h, ql);
 }
 
-template <int D, bool CAUSAL, bool TRACE, bool PERSIST, int NW>
+template <int D, bool CAUSAL, bool TRACE, bool PERSIST, int NW, bool ENTRY = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, TRACE, NW>)))
 void attn_fwd_kernel(AttnArgs a) {
   static_assert(NW == 4 || NW == 8, "4- or 8-wave workgroups");
@@ -229,15 +302,17 @@ void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_v1[D * kBlock];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[32 * NW * D];
   __shared__ __attribute__((aligned(16))) float s_sv[D];
+  __shared__ float s_qmax[NW];
   if (TRACE) {
-    fused_tile<D, CAUSAL, TRACE, NW>(a, a.trace_tile, a.trace_bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    fused_tile<D, CAUSAL, TRACE, NW, ENTRY>(a, a.trace_tile, a.trace_bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv,
+                                            s_qmax);
     return;
   }
   if (!PERSIST) {
     int tile;
     long bh;
     work_item(a, blockIdx.x, tile, bh);
-    fused_tile<D, CAUSAL, TRACE, NW>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    fused_tile<D, CAUSAL, TRACE, NW, ENTRY>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv, s_qmax);
     return;
   }
   // Persistent workgroups take work items from counters (fetch-and-add), one
@@ -267,7 +342,7 @@ void attn_fwd_kernel(AttnArgs a) {
     int tile;
     long bh;
     work_item(a, x + kXcds * k, tile, bh);
-    fused_tile<D, CAUSAL, TRACE, NW>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv);
+    fused_tile<D, CAUSAL, TRACE, NW, ENTRY>(a, tile, bh, s_k0, s_k1, s_v0, s_v1, s_q, s_sv, s_qmax);
     // Every wave is done with the LDS (the epilogue staged its rows in the
     // K/V buffers) and with s_item before the next item refills them.
     __syncthreads();
@@ -335,18 +410,19 @@ __global__ __launch_bounds__(256) void codecs_debug_kernel(const float* __restri
 
 // ------------------------------------------------------------ launchers
 
-template <int D, bool C, bool T, bool P, int NW>
+template <int D, bool C, bool T, bool P, int NW, bool E>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   const long blocks = T ? 1L : P ? (long)a.persist_grid : (long)a.n_qtiles * a.B * a.H;
-  attn_fwd_kernel<D, C, T, P, NW><<<dim3((unsigned)blocks), 64 * NW, 0, stream>>>(a);
+  attn_fwd_kernel<D, C, T, P, NW, E><<<dim3((unsigned)blocks), 64 * NW, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <bool T, bool P, int NW>
+template <bool T, bool P, int NW, bool E = false>
 static hipError_t launch_attn_v(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
   if (D == 128)
-    return causal ? launch_attn_t<128, true, T, P, NW>(a, stream) : launch_attn_t<128, false, T, P, NW>(a, stream);
-  return causal ? launch_attn_t<64, true, T, P, NW>(a, stream) : launch_attn_t<64, false, T, P, NW>(a, stream);
+    return causal ? launch_attn_t<128, true, T, P, NW, E>(a, stream)
+                  : launch_attn_t<128, false, T, P, NW, E>(a, stream);
+  return causal ? launch_attn_t<64, true, T, P, NW, E>(a, stream) : launch_attn_t<64, false, T, P, NW, E>(a, stream);
 }
 
 hipError_t launch_attn_fused(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream) {
@@ -361,8 +437,13 @@ hipError_t launch_attn_persistent(const AttnArgs& a, int D, bool causal, hipStre
   return launch_attn_v<false, true, 4>(a, D, causal, stream);
 }
 
+hipError_t launch_attn_entry(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
+  return launch_attn_v<false, false, 4, true>(a, D, causal, stream);
+}
+
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream) {
   if (kernel == kKernelSplit) return launch_attn_split(a, D, causal, false, stream);
+  if (kernel == kKernelEntry) return launch_attn_entry(a, D, causal, stream);
   if (kernel == kKernelPersistent) return launch_attn_persistent(a, D, causal, stream);
   if (kernel == kKernelWide) return launch_attn_wide(a, D, causal, false, stream);
   return launch_attn_fused(a, D, causal, false, stream);

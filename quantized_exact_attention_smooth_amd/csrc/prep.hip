@@ -318,8 +318,9 @@ __device__ __forceinline__ float head_vscale(const PrepArgs& a, long bh, int c) 
   return m / 448.0f;
 }
 
-// One workgroup per (tensor, 64-row block): job in [0, nqb) codes a Q block,
-// [nqb, nqb + nkb) a K block, [nqb + nkb, nqb + 2 nkb) a V block.
+// One workgroup per (tensor, 64-row block): job in [0, nq) codes a Q block,
+// [nq, nq + nkb) a K block, [nq + nkb, nq + 2 nkb) a V block, with nq = nqb,
+// or 0 when the main loop codes Q itself (skip_q).
 template <int D>
 __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
   __shared__ float s_red[4];
@@ -327,18 +328,19 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
   __shared__ float s_ch[D];  // K channel mean, or V channel scale
   __shared__ float s_rv[D];  // RN(1 / V channel scale)
   // One-dimensional grid (its y extent is capped at 2^16): job-minor.
-  const int n_jobs = a.nqb + 2 * a.nkb;
+  const int nq = a.skip_q ? 0 : a.nqb;
+  const int n_jobs = nq + 2 * a.nkb;
   const int job = (int)(blockIdx.x % n_jobs);
   const long bh = blockIdx.x / n_jobs;
   // The block's data loads are issued before the per-head channel values are
   // read, so the two memory latencies overlap.
-  if (job < a.nqb) {
+  if (job < nq) {
     Int8BlockLoad<D> ld;
     ld.load(a.q + bh * (long)a.Lq * D, a.Lq, job);
     quant_int8_block<D>(ld, a.Lq, job, nullptr, a.q_i8 + bh * (long)a.nqb * kBlock * D,
                         a.q_scale + bh * a.nqb + job, s_red);
-  } else if (job < a.nqb + a.nkb) {
-    const int blk = job - a.nqb;
+  } else if (job < nq + a.nkb) {
+    const int blk = job - nq;
     Int8BlockLoad<D> ld;
     ld.load(a.k + bh * (long)a.Lkv * D, a.Lkv, blk);
     if (threadIdx.x < D) {
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
     quant_int8_block<D>(ld, a.Lkv, blk, s_ch, a.k_i8 + bh * (long)a.nkb * kBlock * D,
                         a.k_scale + bh * a.nkb + blk, s_red);
   } else {
-    const int blk = job - a.nqb - a.nkb;
+    const int blk = job - nq - a.nkb;
     VBlockLoad<D> ld;
     ld.load(a.v + bh * (long)a.Lkv * D, a.Lkv, blk);
     bool tiny = false;
@@ -386,7 +388,7 @@ hipError_t launch_prep(const PrepArgs& args, hipStream_t stream) {
   a.fuse_finalize = ns <= kFuseMaxSplits;
   // The host bounds both flattened grids below 2^31 workgroups.
   const dim3 g_stats((unsigned)((long)ns * BH)), g_fin((unsigned)((long)BH * (a.D / kFinChannels))),
-      g_quant((unsigned)((long)(a.nqb + 2 * a.nkb) * BH));
+      g_quant((unsigned)((long)((a.skip_q ? 0 : a.nqb) + 2 * a.nkb) * BH));
   if (a.D == 128) {
     prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
     hipError_t e = hipGetLastError();

@@ -164,6 +164,7 @@ int resolve_kernel(int kernel, int B, int H, int Lq) {
   if (kernel == SAGE_KERNEL_SPLIT) return sage::kKernelSplit;
   if (kernel == SAGE_KERNEL_PERSISTENT) return sage::kKernelPersistent;
   if (kernel == SAGE_KERNEL_WIDE) return sage::kKernelWide;
+  if (kernel == SAGE_KERNEL_ENTRY) return sage::kKernelEntry;
   return -1;
 }
 
@@ -182,10 +183,11 @@ int check_prep_args(const void* q, const void* k, const void* v, int B, int H, i
   return SAGE_OK;
 }
 
-// Body of sage_quant_prep (also run by sage_attn_fwd on its workspace).
+// Body of sage_quant_prep (also run by sage_attn_fwd on its workspace);
+// skip_q leaves q_i8 and q_scale unwritten.
 int quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq, int Lkv, int D,
                int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean, uint8_t* v_fp8,
-               float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
+               float* v_scale, void* scratch, size_t scratch_bytes, void* stream, bool skip_q = false) {
   const int st = check_prep_args(q, k, v, B, H, Lq, Lkv, D, q_i8, q_scale, k_i8, k_scale, k_mean, v_fp8, v_scale);
   if (st != SAGE_OK) return st;
   if (!scratch || misaligned(scratch, 8)) return SAGE_ERR_INVALID_ARG;
@@ -202,6 +204,7 @@ int quant_prep(const void* q, const void* k, const void* v, int B, int H, int Lq
   a.v_fp8 = v_fp8; a.v_scale = v_scale;
   a.psum = (double*)scratch;
   a.pmax = (float*)((char*)scratch + align_up(n * sizeof(double)));
+  a.skip_q = skip_q ? 1 : 0;
   return hip_status(sage::launch_prep(a, (hipStream_t)stream));
 }
 
@@ -315,7 +318,7 @@ int sage_attn_fwd_prepped_kernel(const int8_t* q_i8, const float* q_scale, const
                            sm_scale, &a);
   if (st != SAGE_OK) return st;
   int kind = resolve_kernel(kernel, B, H, Lq);
-  if (kind < 0) return SAGE_ERR_INVALID_ARG;
+  if (kind < 0 || kind == sage::kKernelEntry) return SAGE_ERR_INVALID_ARG;  // entry: bf16 Q needed
   set_tiles(&a, kind);
   if (kind == sage::kKernelPersistent && !persistent_setup(&a, D, stream, &kind)) return SAGE_ERR_HIP;
   return hip_status(sage::launch_attn(a, D, causal == 1, kind, (hipStream_t)stream));
@@ -337,7 +340,7 @@ int sage_debug_epoch_trace(const int8_t* q_i8, const float* q_scale, const int8_
                            sm_scale, &a);
   if (st != SAGE_OK) return st;
   int kind = resolve_kernel(kernel, B, H, Lq);
-  if (kind < 0) return SAGE_ERR_INVALID_ARG;
+  if (kind < 0 || kind == sage::kKernelEntry) return SAGE_ERR_INVALID_ARG;
   if (kind == sage::kKernelPersistent) kind = sage::kKernelFused;  // the same tile code, traced on one tile
   set_tiles(&a, kind);
   if (b < 0 || b >= B || h < 0 || h >= H || row0 < 0 || row0 >= Lq || row0 % 32 != 0) return SAGE_ERR_INVALID_ARG;
@@ -354,32 +357,47 @@ int sage_debug_epoch_trace(const int8_t* q_i8, const float* q_scale, const int8_
   return hip_status(sage::launch_attn_trace(a, D, causal == 1, kind, (hipStream_t)stream));
 }
 
-int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
-                  int D, int causal, float sm_scale, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+int sage_attn_fwd_kernel(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
+                         int D, int causal, float sm_scale, int kernel, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   const int st = check_dims(B, H, Lq, Lkv, D);
   if (st != SAGE_OK) return st;
   if (!q || !k || !v || !out || !workspace) return SAGE_ERR_INVALID_ARG;
   if (misaligned(workspace, kAlign) || misaligned(out, 16)) return SAGE_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return SAGE_ERR_INVALID_ARG;
-  if (isnan(sm_scale) || isinf(sm_scale)) return SAGE_ERR_INVALID_ARG;
+  int kind = resolve_kernel(kernel, B, H, Lq);
+  if (kind < 0) return SAGE_ERR_INVALID_ARG;
   const Layout l = layout(B, H, Lq, Lkv, D);
   if (workspace_bytes < l.total) return SAGE_ERR_WORKSPACE;
   char* ws = (char*)workspace;
-  // The preparation pass writes every operand into the workspace, then the
-  // main loop runs on them.
-  int s = quant_prep(q, k, v, B, H, Lq, Lkv, D, (int8_t*)(ws + l.q_i8), (float*)(ws + l.q_scale),
-                     (int8_t*)(ws + l.k_i8), (float*)(ws + l.k_scale), (float*)(ws + l.k_mean),
-                     (uint8_t*)(ws + l.v_fp8), (float*)(ws + l.v_scale), ws + l.psum, l.total - l.psum, stream);
+  // Every argument is checked, and the persistent design's counter taken,
+  // before anything is launched.
+  int s = check_prep_args(q, k, v, B, H, Lq, Lkv, D, (int8_t*)(ws + l.q_i8), (float*)(ws + l.q_scale),
+                          (int8_t*)(ws + l.k_i8), (float*)(ws + l.k_scale), (float*)(ws + l.k_mean),
+                          (uint8_t*)(ws + l.v_fp8), (float*)(ws + l.v_scale));
   if (s != SAGE_OK) return s;
   sage::AttnArgs a;
   s = attn_args((const int8_t*)(ws + l.q_i8), (const float*)(ws + l.q_scale), (const int8_t*)(ws + l.k_i8),
-                (const float*)(ws + l.k_scale), (const uint8_t*)(ws + l.v_fp8), (const float*)(ws + l.v_scale),
-                out, B, H, Lq, Lkv, D, causal, sm_scale, &a);
+                    (const float*)(ws + l.k_scale), (const uint8_t*)(ws + l.v_fp8),
+                    (const float*)(ws + l.v_scale), out, B, H, Lq, Lkv, D, causal, sm_scale, &a);
   if (s != SAGE_OK) return s;
-  const int kind = auto_kernel(B, H, Lq);
+  const bool entry = kind == sage::kKernelEntry;
+  if (entry) a.q = (const uint16_t*)q;
   set_tiles(&a, kind);
+  if (kind == sage::kKernelPersistent && !persistent_setup(&a, D, stream, &kind)) return SAGE_ERR_HIP;
+  // The preparation pass writes the operands into the workspace (all but
+  // Q's when the main loop codes Q), then the main loop runs on them.
+  s = quant_prep(q, k, v, B, H, Lq, Lkv, D, (int8_t*)(ws + l.q_i8), (float*)(ws + l.q_scale),
+                 (int8_t*)(ws + l.k_i8), (float*)(ws + l.k_scale), (float*)(ws + l.k_mean),
+                 (uint8_t*)(ws + l.v_fp8), (float*)(ws + l.v_scale), ws + l.psum, l.total - l.psum, stream, entry);
+  if (s != SAGE_OK) return s;
   return hip_status(sage::launch_attn(a, D, causal == 1, kind, (hipStream_t)stream));
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
+                  int D, int causal, float sm_scale, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return sage_attn_fwd_kernel(q, k, v, out, B, H, Lq, Lkv, D, causal, sm_scale, SAGE_KERNEL_AUTO, workspace,
+                              workspace_bytes, stream);
 }
 
 int sage_debug_qk_int32(const int8_t* q_i8, const int8_t* k_i8, int B, int H, int Lq, int Lkv, int D,

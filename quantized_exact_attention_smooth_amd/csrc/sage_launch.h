@@ -26,6 +26,7 @@ struct PrepArgs {
   float* pmax;   // [B*H][n_split][D] channel absmax partials of V
   int n_split;   // statistics splits per head
   int fuse_finalize;  // 1: the quantization workgroups reduce the splits themselves
+  int skip_q;         // 1: Q is not coded (the main loop codes it from q)
 };
 
 struct AttnArgs {
@@ -36,6 +37,7 @@ struct AttnArgs {
   const uint8_t* v_fp8;
   const float* v_scale;
   uint16_t* out;
+  const uint16_t* q;  // bf16 Q [B][H][Lq][D]: the entry design codes it (q_i8, q_scale unused)
   int B, H, Lq, Lkv, nqb, nkb, n_qtiles;
   int grouped;       // 1: head-grouped tile order (not causal, B*H a multiple of 8)
   float scale_log2;  // sm_scale * log2(e)
@@ -67,6 +69,7 @@ constexpr int kKernelFused = 1;  // every wave runs QK, softmax and PV for its r
 constexpr int kKernelSplit = 2;  // softmax waves and PV waves own separate state
 constexpr int kKernelPersistent = 3;  // fused waves in persistent workgroups fed by a work counter
 constexpr int kKernelWide = 4;        // fused waves in 8-wave (256-row) workgroups
+constexpr int kKernelEntry = 5;       // fused waves that code their Q tile from bf16 themselves
 
 // Query rows per workgroup of a main-loop design.
 constexpr int tile_rows(int kernel) { return kernel == kKernelWide ? 256 : kQTile; }
@@ -78,6 +81,7 @@ hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, int kernel, 
 hipError_t launch_attn_fused(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream);
 hipError_t launch_attn_split(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream);
 hipError_t launch_attn_wide(const AttnArgs& a, int D, bool causal, bool trace, hipStream_t stream);
+hipError_t launch_attn_entry(const AttnArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_qk_debug(const QkDebugArgs& a, int D, hipStream_t stream);
 hipError_t launch_codecs_debug(const float* x, int n, uint8_t* p8, uint16_t* bf16, hipStream_t stream);
 

@@ -31,7 +31,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("sage_quant_prep", "sage_quant_prep_noalloc", "sage_attn_fwd", "sage_attn_fwd_prepped",
-              "sage_attn_fwd_prepped_kernel",
+              "sage_attn_fwd_prepped_kernel", "sage_attn_fwd_kernel",
               "sage_workspace_bytes",
               "sage_prep_scratch_bytes", "sage_debug_qk_int32", "sage_debug_codecs", "sage_debug_epoch_trace",
               "sage_status_str"):
@@ -100,6 +100,14 @@ def test_attn_fwd_rejects_bad_arguments_without_touching_the_gpu(lib):
     odd = ctypes.c_void_p((1 << 20) + 8)
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 128, 128, 128, 0, 0.0, odd, need, None) == -1
     assert f(FAKE, FAKE, FAKE, odd, 1, 2, 128, 128, 128, 0, 0.0, FAKE, need, None) == -1
+    g = lib.sage_attn_fwd_kernel  # every design value and argument checked before any launch
+    for design in (-1, 6):
+        assert g(FAKE, FAKE, FAKE, FAKE, 1, 2, 128, 128, 128, 0, 0.0, design, FAKE, need, None) == -1
+    for design in range(6):
+        assert g(FAKE, FAKE, FAKE, FAKE, 1, 2, 128, 128, 128, 0, 0.0, design, FAKE, need - 1, None) == -3
+        assert g(FAKE, FAKE, FAKE, FAKE, 1, 2, 128, 128, 128, 2, 0.0, design, FAKE, need, None) == -1
+        assert g(odd, FAKE, FAKE, FAKE, 1, 2, 128, 128, 128, 0, 0.0, design, FAKE, need, None) == -1
+        assert g(FAKE, FAKE, FAKE, FAKE, 1, 2, 128, 128, 96, 0, 0.0, design, FAKE, need, None) == -2
 
 
 def test_prep_and_prepped_reject_bad_arguments(lib):
@@ -123,7 +131,8 @@ def test_prep_and_prepped_reject_bad_arguments(lib):
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 0, 0.0, None) == -2
     assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 3, 0.0, None) == -1
     k = lib.sage_attn_fwd_prepped_kernel
-    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, 5, None) == -1   # unknown design
+    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, 5, None) == -1   # entry: bf16 Q
+    assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, 6, None) == -1   # unknown design
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, -1, None) == -1
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 64, 0, 0.0, 2, None) == -1
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 0, 0.0, 1, None) == -2
@@ -143,5 +152,6 @@ def test_debug_qk_rejects_out_of_range_tiles(lib):
     assert t(*ok, 1, 0, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == -1     # row0 >= Lq
     assert t(*ok, 1, 0, 0, 0, None, FAKE, FAKE, FAKE, None) == -1       # missing stats
     assert t(*ok, 2, 0, 0, 0, FAKE, FAKE, None, FAKE, None) == -1       # missing pv
-    assert t(*ok, 5, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1       # unknown design
+    assert t(*ok, 5, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1       # entry design: not traced
+    assert t(*ok, 6, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1       # unknown design
     assert lib.sage_debug_codecs(FAKE, 0, FAKE, FAKE, None) == 0

@@ -1,6 +1,10 @@
 """The other main-loop designs against the oracle and against the fused
-design: the wave-specialised one (SAGE_KERNEL_SPLIT) and the persistent one
-(SAGE_KERNEL_PERSISTENT, fused waves in workgroups fed by a work counter).
+design: the wave-specialised one (SAGE_KERNEL_SPLIT), the persistent one
+(SAGE_KERNEL_PERSISTENT, fused waves in workgroups fed by a work counter),
+the wide one (SAGE_KERNEL_WIDE, 8-wave workgroups) and the entry one
+(SAGE_KERNEL_ENTRY, whole-path calls only: the main loop codes Q from bf16
+itself, with the preparation pass's arithmetic, so the codes and therefore
+the outputs are the same bits).
 
 Every design runs the same per-epoch arithmetic in the same order (the same
 P bytes, the same rescale and matrix-core accumulation of RO, the same
@@ -21,7 +25,9 @@ from _parity import assert_out_close, oracle_preps, oracle_rows, say
 pytestmark = pytest.mark.gpu
 
 FUSED = sage.SAGE_KERNEL_FUSED
-DESIGNS = {"split": sage.SAGE_KERNEL_SPLIT, "persistent": sage.SAGE_KERNEL_PERSISTENT, "wide": sage.SAGE_KERNEL_WIDE}
+ENTRY = sage.SAGE_KERNEL_ENTRY
+DESIGNS = {"split": sage.SAGE_KERNEL_SPLIT, "persistent": sage.SAGE_KERNEL_PERSISTENT, "wide": sage.SAGE_KERNEL_WIDE,
+           "entry": ENTRY}
 
 
 @pytest.fixture(params=sorted(DESIGNS))
@@ -30,9 +36,14 @@ def design(request):
 
 
 def _both(q, k, v, causal, sm_scale, dev, design):
-    pr = sage.quant_prep(q.to(dev), k.to(dev), v.to(dev))
-    a = sage.attn_fwd_prepped(pr, causal, sm_scale, kernel=FUSED)
-    b = sage.attn_fwd_prepped(pr, causal, sm_scale, kernel=design)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    if design == ENTRY:  # a whole-path design: both sides start from the bf16 inputs
+        a = sage.attn_fwd(qd, kd, vd, causal, sm_scale, kernel=FUSED)
+        b = sage.attn_fwd(qd, kd, vd, causal, sm_scale, kernel=ENTRY)
+    else:
+        pr = sage.quant_prep(qd, kd, vd)
+        a = sage.attn_fwd_prepped(pr, causal, sm_scale, kernel=FUSED)
+        b = sage.attn_fwd_prepped(pr, causal, sm_scale, kernel=design)
     torch.cuda.synchronize()
     return si.bf16_bits(a), si.bf16_bits(b)
 
@@ -100,14 +111,52 @@ def test_design_equals_fused_on_seeded_random_shapes(seed, design, gpu_device):
 
 def test_design_repeated_launches_are_bit_identical(design, gpu_device):
     w = si.WORKLOADS[2]
-    q, k, v = si.workload_qkv(w)
-    pr = sage.quant_prep(q.to(gpu_device), k.to(gpu_device), v.to(gpu_device))
-    first = si.bf16_bits(sage.attn_fwd_prepped(pr, w.causal, w.sm_scale, kernel=design))
+    q, k, v = (t.to(gpu_device) for t in si.workload_qkv(w))
     out = torch.empty((w.B, w.H, w.Lq, w.D), dtype=torch.bfloat16, device=gpu_device)
+    if design == ENTRY:
+        ws = torch.empty(sage.workspace_bytes(w.B, w.H, w.Lq, w.Lkv, w.D), dtype=torch.uint8, device=gpu_device)
+        run = lambda o: sage.attn_fwd(q, k, v, w.causal, w.sm_scale, out=o, workspace=ws, kernel=ENTRY)  # noqa: E731
+    else:
+        pr = sage.quant_prep(q, k, v)
+        run = lambda o: sage.attn_fwd_prepped(pr, w.causal, w.sm_scale, out=o, kernel=design)  # noqa: E731
+    first = si.bf16_bits(run(None))
     for i in range(50):
-        sage.attn_fwd_prepped(pr, w.causal, w.sm_scale, out=out, kernel=design)
+        run(out)
     torch.cuda.synchronize()
     assert np.array_equal(si.bf16_bits(out), first)
+
+
+def test_entry_codes_q_blocks_at_the_scale_edges(gpu_device):
+    """Q blocks that reach the corners of the INT8 step: an all-zero block
+    (scale 0, every code 0), a block whose scale is below 2^-60 (the quotient
+    is taken by division), one of subnormal bf16 values, one of very large
+    values, and blocks whose second 32-row half lies past Lq (the absmax of
+    the rows below Lq alone sets the scale). The entry design must give the
+    fused design's bits, and both the oracle's values."""
+    B, H, D = 1, 2, 128
+    sc = 1 / math.sqrt(D)
+    for Lq in (33, 64 * 7 + 20):
+        q, k, v = si.make_qkv(B, H, Lq, 300, D, "normal", 2.0, seed=4000 + Lq)
+        q = q.clone()
+        if Lq > 64:
+            q[:, :, 0:64] = 0.0                  # block 0: all zero
+            q[:, :, 64:128] *= 1e-30             # block 1: scale ~ 1e-30 / 127 < 2^-60
+            q[:, :, 128:192] *= 1e-39            # block 2: subnormal bf16 values
+            q[:, 0, 192:256] *= 1e30             # block 3: very large values (scores stay finite)
+            q[:, :, 256:320, ::3] = 0.0
+        for causal in (False, True):
+            say(f"entry vs fused at the Q scale edges: Lq {Lq} causal {causal}")
+            fused, entry = _both(q, k, v, causal, sc, gpu_device, ENTRY)
+            assert np.array_equal(fused, entry), (Lq, causal)
+            for (b, h), o in oracle_preps(q, k, v, [(0, 0), (0, 1)]).items():
+                assert_out_close(entry[b, h], oracle_rows(o, causal, sc, 0, Lq), f"entry: scale edges {(b, h)}")
+    # The largest bf16 magnitudes code to +-127 with a scale near 2.7e36; the
+    # scores then overflow fp32, so only the two designs are compared.
+    q, k, v = si.make_qkv(1, 1, 100, 100, D, "normal", 2.0, seed=4100)
+    q = q.clone()
+    q[:, :, :64] = torch.finfo(torch.bfloat16).max * torch.sign(q[:, :, :64])
+    fused, entry = _both(q, k, v, True, sc, gpu_device, ENTRY)
+    assert np.array_equal(fused, entry)
 
 
 def test_persistent_counter_returns_to_zero_across_streams_and_shapes(gpu_device):
