@@ -70,10 +70,13 @@ __device__ __forceinline__ int pack4_fp8(float x0, float x1, float x2, float x3)
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
-// Two fp32 values -> two bf16 (x0 in the low half), round to nearest even.
+// Two fp32 values -> two bf16 (x0 in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 (two scalar conversions would each fill half a
+// register and need a shift and an or to combine).
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2_bf16(float x0, float x1) {
-  __bf16 b0 = (__bf16)x0, b1 = (__bf16)x1;
-  return (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x0, x1}, v2bf));
 }
 
 // Direct global -> LDS copies (no staging registers) through buffer loads:
@@ -361,6 +364,20 @@ __device__ __forceinline__ void pv_epoch(const uint8_t* v_cur, const v8i& pb, v1
     const v4i hi = *reinterpret_cast<const v4i*>(v_cur + v_lds_off(ch, 2 * h + 1));
     const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     ro[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, ro[cb], 0, 0, 0, 127, 0, 127);
+  }
+}
+
+// The first epoch's PV step: RO = PV, the accumulator operand a zero
+// constant (RO needs no clearing, and 0 * alpha + PV is PV exactly).
+template <int D>
+__device__ __forceinline__ void pv_epoch_first(const uint8_t* v_cur, const v8i& pb, v16f* ro, int h, int ql) {
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+    const int ch = 32 * cb + ql;
+    const v4i lo = *reinterpret_cast<const v4i*>(v_cur + v_lds_off(ch, 2 * h));
+    const v4i hi = *reinterpret_cast<const v4i*>(v_cur + v_lds_off(ch, 2 * h + 1));
+    const v8i av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    ro[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pb, v16f{}, 0, 0, 0, 127, 0, 127);
   }
 }
 

@@ -227,16 +227,19 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
   for (int s = 0; s < D / 32; ++s) asm volatile("" : "+v"(koff[s]));
 
   float m = -INFINITY, l = 0.0f;
+  // RO is first written by epoch 0's PV step (a wave that computes any epoch
+  // computes epoch 0: every row that sees a key sees key 0); a wave with no
+  // epoch clears it after the loop.
   v16f ro[D / 32];
-#pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) ro[cb] = v16f{};
   __builtin_amdgcn_s_waitcnt(0);  // the first fills (issued above) have landed
   __syncthreads();
 
   // One epoch. The epoch's parity is a template argument so every LDS buffer
-  // is a fixed object.
-  auto body = [&](auto parity, const int e) {
+  // is a fixed object; epoch 0 (first) has its own copy, with no rescale and
+  // a zero accumulator for its PV step.
+  auto body = [&](auto parity, auto first, const int e) {
     constexpr int P = decltype(parity)::value;
+    constexpr bool F = decltype(first)::value;
     uint8_t* k_cur = P ? s_k1 : s_k0;   // K(e)
     uint8_t* v_cur = P ? s_v1 : s_v0;   // V(e)
     uint8_t* k_fill = P ? s_k0 : s_k1;  // K(e+1) replaces K(e-1)
@@ -257,11 +260,14 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
       bool moved;
       softmax_epoch(acc0, acc1, c, masked, dlim, kBlock * e <= lim, m, l, pb, alpha, moved);
       // Per-tile rescale; a no-op (alpha == 1 in every lane) when no row max moved.
-      if (moved) {
+      if (!F && moved) {
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) ro[cb] *= alpha;
       }
-      pv_epoch<D>(v_cur, pb, ro, h, ql);
+      if (F)
+        pv_epoch_first<D>(v_cur, pb, ro, h, ql);
+      else
+        pv_epoch<D>(v_cur, pb, ro, h, ql);
       if (TRACE && w == a.trace_wave) {
         // The epoch's own PV partial, run again into a zeroed accumulator.
         v16f pv[D / 32];
@@ -276,9 +282,18 @@ __device__ __forceinline__ void fused_tile(const AttnArgs& a, const int tile, co
     __syncthreads();
   };
 
-  for (int e = 0; e < n_ep; e += 2) {
-    body(std::integral_constant<int, 0>{}, e);
-    if (e + 1 < n_ep) body(std::integral_constant<int, 1>{}, e + 1);
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  using First = std::true_type;
+  using Later = std::false_type;
+  if (n_ep > 0) body(Even{}, First{}, 0);
+  for (int e = 1; e < n_ep; e += 2) {
+    body(Odd{}, Later{}, e);
+    if (e + 1 < n_ep) body(Even{}, Later{}, e + 1);
+  }
+  if (w_ep == 0) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) ro[cb] = v16f{};
   }
 
   // Epilogue: the two halves of a query hold partial sums of l. Each wave
