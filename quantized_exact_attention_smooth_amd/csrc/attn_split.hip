@@ -98,16 +98,18 @@ void attn_split_kernel(AttnArgs a) {
     if (n_ep > 1) k_tile_to_lds<D>(krs, kBlock * D, s_k1, g, lane);
     const int ti = threadIdx.x - 256;
     if (ti < D) s_sv[ti] = a.v_scale[bh * D + ti];
+    // RO is first written by epoch 0's PV step (a group that computes any
+    // epoch computes epoch 0); a group with no epoch clears it after the loop.
     v16f ro[D / 32];
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) ro[cb] = v16f{};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // K(0), K(1) resident
     __syncthreads();  // the softmax waves have read K(0): its slot may refill
 
-    // Period t: copies of K(t+2) and V(t), then the PV step of epoch t - 1.
-    auto body = [&](auto parity, const int t) {
+    // Period t: copies of K(t+2) and V(t), then the PV step of epoch t - 1
+    // (period 1, first, holds epoch 0's: no rescale, a zero accumulator).
+    auto body = [&](auto parity, auto first, const int t) {
       constexpr int P = decltype(parity)::value;
+      constexpr bool F = decltype(first)::value;
       uint8_t* k_fill = P ? s_k1 : s_k0;         // K(t+2) replaces K(t)
       uint8_t* v_fill = P ? s_v1 : s_v0;         // V(t) replaces V(t-2)
       const uint8_t* v_cur = P ? s_v0 : s_v1;    // V(t-1)
@@ -123,11 +125,14 @@ void attn_split_kernel(AttnArgs a) {
         const float alpha = a_cur[g * 32 + ql];
         // Per-tile rescale; a no-op (alpha == 1 in every lane) when no row
         // max of the group moved.
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+        if (!F && __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
           for (int cb = 0; cb < D / 32; ++cb) ro[cb] *= alpha;
         }
-        pv_epoch<D>(v_cur, pb, ro, h, ql);
+        if (F)
+          pv_epoch_first<D>(v_cur, pb, ro, h, ql);
+        else
+          pv_epoch<D>(v_cur, pb, ro, h, ql);
         if (TRACE && g == a.trace_wave) {
           v16f pv[D / 32];
 #pragma unroll
@@ -139,9 +144,17 @@ void attn_split_kernel(AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
-    for (int t = 0; t <= n_ep; t += 2) {
-      body(std::integral_constant<int, 0>{}, t);
-      if (t + 1 <= n_ep) body(std::integral_constant<int, 1>{}, t + 1);
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    body(Even{}, std::false_type{}, 0);
+    if (1 <= n_ep) body(Odd{}, std::true_type{}, 1);
+    for (int t = 2; t <= n_ep; t += 2) {
+      body(Even{}, std::false_type{}, t);
+      if (t + 1 <= n_ep) body(Odd{}, std::false_type{}, t + 1);
+    }
+    if (w_ep == 0) {
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) ro[cb] = v16f{};
     }
     __syncthreads();  // 1/l of every row is in s_rcp
     const float rcp = s_rcp[g * 32 + ql];
