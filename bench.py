@@ -1,9 +1,9 @@
 """Throughput of the quantized attention path on one MI355X.
 
 One step = the whole path on one batch: sage_attn_fwd, the user-facing call
-(K mean, smoothing, INT8 Q and K blocks and FP8 V in the preparation pass,
-then the fused main loop), on inputs already resident in HBM. Prints one
-JSON line.
+(K mean, smoothing, INT8 K blocks and FP8 V in the preparation pass, and the
+main loop, which on full grids codes the INT8 Q blocks itself), on inputs
+already resident in HBM. Prints one JSON line.
 
   value     whole-step throughput in TOPS, ops = 4*B*H*Lq*Lkv*D (halved when
             causal), over the wall time of K steps between two device syncs;
@@ -11,7 +11,9 @@ JSON line.
             (K back-to-back launches between two HIP events recorded on the
             stream the kernels run on), against the dense INT8/FP8
             matrix-core peak of MI355X (5.0 POPS);
-  scopes    main (sage_attn_fwd_prepped), prep (sage_quant_prep) and
+  scopes    main (the step's main kernel alone: sage_attn_fwd_kv_prepped for
+            the entry design, else sage_attn_fwd_prepped), prep (its
+            preparation pass: sage_quant_prep_kv, else sage_quant_prep) and
             end-to-end (sage_attn_fwd, the user-facing call) each timed as
             back-to-back launches; main also as the p50 and coefficient of
             variation of 10 batches of 20 launches and as the p50 of 2000
@@ -238,9 +240,9 @@ def main() -> int:
     ap.add_argument("--shape", type=str, default=None,
                     help="B,H,Lq,Lkv,D,causal: a custom N(0,1) workload (K offset sigma 2) instead of a named one")
     ap.add_argument("--kernel", choices=("auto", "fused", "split", "persistent", "wide", "entry"), default="auto",
-                    help="main-loop design timed in the main scope (sage_attn_fwd uses auto); entry, which "
-                         "codes Q inside the main kernel, exists for the whole path only: it replaces both the "
-                         "main and the end-to-end scope")
+                    help="main-loop design timed in the main scope; auto times the design sage_attn_fwd selects "
+                         "for the shape (sage_auto_design), the others that design (the end-to-end scope stays "
+                         "sage_attn_fwd, except for entry, which times sage_attn_fwd_kernel with it)")
     ap.add_argument("--single-samples", type=int, default=2000,
                     help="single launches timed for the main kernel's single-launch p50 (fewer under a profiler)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -289,6 +291,11 @@ def main() -> int:
     causal = int(w.causal)
 
     def prep():
+        if entry:  # the entry design's preparation: K and V only
+            _lib.check("sage_quant_prep_kv", L.sage_quant_prep_kv(
+                k.data_ptr(), v.data_ptr(), B, H, Lkv, D, k8.data_ptr(), kscale.data_ptr(), kmean.data_ptr(),
+                v8.data_ptr(), vscale.data_ptr(), scratch.data_ptr(), n.value, sp))
+            return
         _lib.check("sage_quant_prep", L.sage_quant_prep(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Lq, Lkv, D, q8.data_ptr(), qs.data_ptr(),
             k8.data_ptr(), kscale.data_ptr(), kmean.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
@@ -297,12 +304,27 @@ def main() -> int:
     kernel = {"auto": _lib.SAGE_KERNEL_AUTO, "fused": _lib.SAGE_KERNEL_FUSED, "split": _lib.SAGE_KERNEL_SPLIT,
               "persistent": _lib.SAGE_KERNEL_PERSISTENT, "wide": _lib.SAGE_KERNEL_WIDE,
               "entry": _lib.SAGE_KERNEL_ENTRY}[args.kernel]
-    entry = kernel == _lib.SAGE_KERNEL_ENTRY
+    # The design whose main kernel the main scope times: with auto, the one the
+    # whole path (the timed step) runs for this shape.
+    design = kernel
+    if kernel == _lib.SAGE_KERNEL_AUTO:
+        d = ctypes.c_int(-1)
+        _lib.check("sage_auto_design", L.sage_auto_design(B, H, Lq, Lkv, D, 1, ctypes.byref(d)))
+        design = d.value
+    design_name = {_lib.SAGE_KERNEL_FUSED: "fused", _lib.SAGE_KERNEL_SPLIT: "split",
+                   _lib.SAGE_KERNEL_PERSISTENT: "persistent", _lib.SAGE_KERNEL_WIDE: "wide",
+                   _lib.SAGE_KERNEL_ENTRY: "entry"}[design]
+    entry = design == _lib.SAGE_KERNEL_ENTRY
 
     def main_loop():
+        if entry:  # bf16 Q against the prepared K/V: the entry design's main kernel
+            _lib.check("sage_attn_fwd_kv_prepped", L.sage_attn_fwd_kv_prepped(
+                q.data_ptr(), k8.data_ptr(), kscale.data_ptr(), v8.data_ptr(), vscale.data_ptr(), out.data_ptr(),
+                B, H, Lq, Lkv, D, causal, w.sm_scale, sp))
+            return
         _lib.check("sage_attn_fwd_prepped_kernel", L.sage_attn_fwd_prepped_kernel(
             q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), kscale.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
-            out.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale, kernel, sp))
+            out.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale, design, sp))
 
     # end-to-end: sage_attn_fwd into a preallocated workspace
     nws = ctypes.c_size_t(0)
@@ -311,7 +333,7 @@ def main() -> int:
     out_e2e = torch.empty_like(out)
 
     def e2e():
-        if entry:
+        if kernel == _lib.SAGE_KERNEL_ENTRY:
             _lib.check("sage_attn_fwd_kernel", L.sage_attn_fwd_kernel(
                 q.data_ptr(), k.data_ptr(), v.data_ptr(), out_e2e.data_ptr(), B, H, Lq, Lkv, D, causal,
                 w.sm_scale, kernel, ws.data_ptr(), nws.value, sp))
@@ -319,9 +341,6 @@ def main() -> int:
         _lib.check("sage_attn_fwd", L.sage_attn_fwd(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out_e2e.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale,
             ws.data_ptr(), nws.value, sp))
-
-    if entry:  # the entry design's main kernel runs only inside the whole path
-        main_loop = e2e
 
     for _ in range(args.warmup):
         e2e()
@@ -387,19 +406,21 @@ def main() -> int:
     achieved = ops / (main_avg * 1e-3) / 1e12
     prof = _profile(w.name, args.kernel)
     traffic = prof.get("bytes_per_launch")
-    prep_bytes = B * H * (Lq + 2 * Lkv) * D * 2 + B * H * (nqb + 2 * nkb) * 64 * D
+    # algorithmic bytes of the preparation scope: bf16 inputs read once, codes written
+    prep_bytes = (B * H * 2 * Lkv * D * 2 + B * H * 2 * nkb * 64 * D if entry else
+                  B * H * (Lq + 2 * Lkv) * D * 2 + B * H * (nqb + 2 * nkb) * 64 * D)
 
     rec = {
         "metric": METRIC, "value": ops / (ms_step * 1e-3) / 1e12, "unit": "TOPS", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int8+fp8_e4m3", "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "Lq": Lq, "Lkv": Lkv, "D": D, "causal": w.causal,
-                   "k_offset_sigma": w.k_offset_sigma, "dist": w.dist, "main_kernel": args.kernel},
+                   "k_offset_sigma": w.k_offset_sigma, "dist": w.dist, "main_kernel": design_name},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TOPS, "unit": "TOPS",
                      "frac": achieved / PEAK_TOPS, "traffic": traffic,
-                     "scope": ("whole path of the entry design (sage_attn_fwd_kernel: the Q step runs inside "
-                               "the main kernel); value is the whole step") if entry else
-                              "main kernel (sage_attn_fwd_prepped); value is the whole step",
+                     "scope": ("main kernel of the entry design (sage_attn_fwd_kv_prepped: bf16 Q coded in "
+                               "the loop); value is the whole step" if entry else
+                               "main kernel (sage_attn_fwd_prepped); value is the whole step"),
                      "e2e_frac": ops / (e2e_avg * 1e-3) / 1e12 / PEAK_TOPS,
                      "hbm_GBps": traffic / (main_avg * 1e-3) / 1e9 if traffic else None,
                      "mfma_busy": prof.get("mfma_busy"), "valu_busy": prof.get("valu_busy"),

@@ -161,14 +161,18 @@ int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t
  *                      codes K and V only, and each workgroup reads its 128
  *                      rows of bf16 Q and codes them straight into its LDS Q
  *                      tile with the preparation pass's arithmetic (the same
- *                      codes and scales), so Q codes never pass through
- *                      memory; the workspace's Q code and Q scale areas are
- *                      left unwritten. Calls on prepared operands return
- *                      SAGE_ERR_INVALID_ARG for it.
+ *                      codes and scales for finite inputs), so Q codes
+ *                      never pass through memory; the workspace's Q code and
+ *                      Q scale areas are left unwritten. Its two stages are
+ *                      also public: sage_quant_prep_kv and
+ *                      sage_attn_fwd_kv_prepped. Calls on prepared Q codes
+ *                      return SAGE_ERR_INVALID_ARG for it.
  *   SAGE_KERNEL_AUTO   the design measured faster for the shape: SPLIT when
  *                      B*H*ceil(Lq/128) < 256 (fewer 128-row tiles than
- *                      compute units), FUSED otherwise. sage_attn_fwd and
- *                      sage_attn_fwd_prepped use it.
+ *                      compute units); otherwise FUSED for calls on prepared
+ *                      operands and ENTRY for the whole path (sage_attn_fwd),
+ *                      where it is faster end to end. sage_auto_design
+ *                      reports the choice.
  */
 enum sage_kernel {
     SAGE_KERNEL_AUTO = 0,
@@ -190,10 +194,14 @@ int sage_attn_fwd_prepped_kernel(const int8_t* q_i8, const float* q_scale, const
                                  void* stream);
 
 /*
- * The whole path: sage_quant_prep into the workspace (its parts laid out as
- * sage_workspace_bytes describes), then sage_attn_fwd_prepped on them, both
- * on stream. workspace: device memory of at least sage_workspace_bytes,
- * 256-byte aligned; it is overwritten.
+ * The whole path with the automatic design (SAGE_KERNEL_AUTO): the
+ * preparation pass into the workspace (its parts laid out as
+ * sage_workspace_bytes describes), then the main loop on them, both on
+ * stream. On full grids that is sage_quant_prep_kv + sage_attn_fwd_kv_prepped
+ * (the entry design), otherwise sage_quant_prep + sage_attn_fwd_prepped; the
+ * output is the same bits either way for finite inputs. workspace: device
+ * memory of at least sage_workspace_bytes, 256-byte aligned; it is
+ * overwritten.
  */
 int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
                   int D, int causal, float sm_scale, void* workspace, size_t workspace_bytes,
@@ -207,6 +215,39 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
 int sage_attn_fwd_kernel(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,
                          int D, int causal, float sm_scale, int kernel, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * The K/V half of the preparation pass (Experiment Log, "Phase 0 Import And
+ * Verification": K smoothing, INT8 quantization, FP8 V), e.g. for a key and
+ * value set that several query batches attend to: k_mean, k_i8, k_scale,
+ * v_fp8 and v_scale exactly as sage_quant_prep writes them for the same k and
+ * v. scratch: at least sage_prep_scratch_bytes for these B, H, Lkv, D (any
+ * Lq). Arguments otherwise as sage_quant_prep.
+ */
+int sage_quant_prep_kv(const void* k, const void* v, int B, int H, int Lkv, int D, int8_t* k_i8, float* k_scale,
+                       float* k_mean, uint8_t* v_fp8, float* v_scale, void* scratch, size_t scratch_bytes,
+                       void* stream);
+
+/*
+ * The main loop of the entry design (SAGE_KERNEL_ENTRY) on K/V prepared by
+ * sage_quant_prep_kv (or sage_quant_prep) and bf16 q [B][H][Lq][D] (16-byte
+ * aligned): each workgroup codes its Q rows itself (Experiment Log, "Closed
+ * Prior Work": the P1 entry fusion inside the attention pipeline), with the
+ * arithmetic of the preparation pass, so for finite inputs the output equals
+ * sage_quant_prep + sage_attn_fwd_prepped bit for bit. Other arguments as
+ * sage_attn_fwd_prepped.
+ */
+int sage_attn_fwd_kv_prepped(const void* q, const int8_t* k_i8, const float* k_scale, const uint8_t* v_fp8,
+                             const float* v_scale, void* out, int B, int H, int Lq, int Lkv, int D, int causal,
+                             float sm_scale, void* stream);
+
+/*
+ * The design SAGE_KERNEL_AUTO selects for a shape: *design =
+ * SAGE_KERNEL_SPLIT, _FUSED or _ENTRY; whole_path = 1 for sage_attn_fwd,
+ * 0 for sage_attn_fwd_prepped. Invalid shapes return the status the calls
+ * would.
+ */
+int sage_auto_design(int B, int H, int Lq, int Lkv, int D, int whole_path, int* design);
 
 /*
  * Debug: the exact int32 QK accumulators of chosen 64x64 tiles, computed by

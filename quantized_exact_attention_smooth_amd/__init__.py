@@ -16,7 +16,8 @@ from ._lib import (LIB_PATH, SAGE_BLOCK, SAGE_KERNEL_AUTO, SAGE_KERNEL_ENTRY, SA
                    SAGE_KERNEL_PERSISTENT, SAGE_KERNEL_SPLIT, SAGE_KERNEL_WIDE, SageError, check, lib,
                    status_str)
 
-__all__ = ["workspace_bytes", "prep_scratch_bytes", "quant_prep", "attn_fwd_prepped", "attn_fwd",
+__all__ = ["workspace_bytes", "prep_scratch_bytes", "quant_prep", "attn_fwd_prepped", "attn_fwd", "quant_prep_kv",
+           "attn_fwd_kv_prepped", "auto_design",
            "debug_qk_int32", "debug_codecs", "debug_epoch_trace", "SageError", "status_str", "LIB_PATH",
            "SAGE_KERNEL_AUTO", "SAGE_KERNEL_FUSED", "SAGE_KERNEL_SPLIT", "SAGE_KERNEL_PERSISTENT", "SAGE_KERNEL_WIDE",
            "SAGE_KERNEL_ENTRY"]
@@ -81,6 +82,58 @@ def quant_prep(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, stream=None) -
     r["_scratch"] = scratch  # keep alive until the stream is done with it
     r["shape"] = (B, H, Lq, Lkv, D)
     return r
+
+
+def quant_prep_kv(k: torch.Tensor, v: torch.Tensor, stream=None) -> dict:
+    """sage_quant_prep_kv: the K/V half of quant_prep. Returns dict of k_i8,
+    k_scale, k_mean, v_fp8 ([B, H, NKB, D, 64] uint8), v_scale and
+    kv_shape (B, H, Lkv, D)."""
+    if k.dim() != 4 or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, H, Lkv, D] of one shape")
+    B, H, Lkv, D = k.shape
+    nkb = -(-Lkv // SAGE_BLOCK)
+    dev = k.device
+    r = dict(k_i8=torch.empty((B, H, nkb * SAGE_BLOCK, D), dtype=torch.int8, device=dev),
+             k_scale=torch.empty((B, H, nkb), dtype=torch.float32, device=dev),
+             k_mean=torch.empty((B, H, D), dtype=torch.float32, device=dev),
+             v_fp8=torch.empty((B, H, nkb, D, SAGE_BLOCK), dtype=torch.uint8, device=dev),
+             v_scale=torch.empty((B, H, D), dtype=torch.float32, device=dev))
+    nbytes = prep_scratch_bytes(B, H, 1, Lkv, D)
+    scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().sage_quant_prep_kv(_dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"), B, H, Lkv, D,
+                                  r["k_i8"].data_ptr(), r["k_scale"].data_ptr(), r["k_mean"].data_ptr(),
+                                  r["v_fp8"].data_ptr(), r["v_scale"].data_ptr(), scratch.data_ptr(), nbytes,
+                                  _stream(stream))
+    check("sage_quant_prep_kv", st)
+    r["_scratch"] = scratch
+    r["kv_shape"] = (B, H, Lkv, D)
+    return r
+
+
+def attn_fwd_kv_prepped(q: torch.Tensor, kv: dict, causal: bool, sm_scale: float = None,
+                        out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """sage_attn_fwd_kv_prepped: bf16 q [B, H, Lq, D] against the K/V operands
+    of quant_prep_kv (or quant_prep), Q coded inside the main loop."""
+    B, H, Lkv, D = kv["kv_shape"] if "kv_shape" in kv else (*kv["shape"][:2], *kv["shape"][3:])
+    if q.dim() != 4 or q.shape[0] != B or q.shape[1] != H or q.shape[3] != D:
+        raise ValueError("q must be [B, H, Lq, D] matching the prepared K/V")
+    Lq = q.shape[2]
+    if out is None:
+        out = torch.empty((B, H, Lq, D), dtype=torch.bfloat16, device=q.device)
+    st = lib().sage_attn_fwd_kv_prepped(
+        _dev(q, torch.bfloat16, "q"), _dev(kv["k_i8"], torch.int8, "k_i8"),
+        _dev(kv["k_scale"], torch.float32, "k_scale"), _dev(kv["v_fp8"], torch.uint8, "v_fp8"),
+        _dev(kv["v_scale"], torch.float32, "v_scale"), _dev(out, torch.bfloat16, "out"), B, H, Lq, Lkv, D,
+        int(bool(causal)), float(sm_scale) if sm_scale else 0.0, _stream(stream))
+    check("sage_attn_fwd_kv_prepped", st)
+    return out
+
+
+def auto_design(B: int, H: int, Lq: int, Lkv: int, D: int, whole_path: bool = True) -> int:
+    """sage_auto_design: the SAGE_KERNEL_* value SAGE_KERNEL_AUTO selects."""
+    d = ctypes.c_int(-1)
+    check("sage_auto_design", lib().sage_auto_design(B, H, Lq, Lkv, D, int(bool(whole_path)), ctypes.byref(d)))
+    return d.value
 
 
 def attn_fwd_prepped(prep: dict, causal: bool, sm_scale: float = None, out: torch.Tensor = None,

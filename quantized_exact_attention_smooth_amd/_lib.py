@@ -54,6 +54,12 @@ def lib() -> ctypes.CDLL:
             L.sage_attn_fwd.restype = I
             L.sage_attn_fwd_kernel.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
             L.sage_attn_fwd_kernel.restype = I
+            L.sage_quant_prep_kv.argtypes = [P, P, I, I, I, I, P, P, P, P, P, P, Z, P]
+            L.sage_quant_prep_kv.restype = I
+            L.sage_attn_fwd_kv_prepped.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, P]
+            L.sage_attn_fwd_kv_prepped.restype = I
+            L.sage_auto_design.argtypes = [I, I, I, I, I, I, ctypes.POINTER(I)]
+            L.sage_auto_design.restype = I
             L.sage_debug_qk_int32.argtypes = [P, P, I, I, I, I, I, P, I, P, P]
             L.sage_debug_qk_int32.restype = I
             L.sage_debug_codecs.argtypes = [P, I, P, P, P]

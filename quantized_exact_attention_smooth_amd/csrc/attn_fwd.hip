@@ -80,13 +80,22 @@ struct FusedLds {
 };
 
 // Entry design: the Q codes of a tile, made by the main loop from the bf16
-// rows exactly as the preparation pass makes them (an INT8 scale per 64-row
-// block: s = absmax / 127 over the block's rows < Lq; code = clamp(rint(x /
-// s), +-127) with the quotient rounded as an IEEE division; rows >= Lq code
-// 0), so the codes and scales are the same bits. Each wave codes its own 32
-// rows (wrow0 ..) into the LDS Q tile; the two waves of a 64-row block
-// exchange their absmax through s_qmax (one slot per wave). Every wave of
-// the workgroup calls it (it holds a barrier). Returns the block's s.
+// rows as the preparation pass makes them (an INT8 scale per 64-row block:
+// s = absmax / 127 over the block's rows < Lq; code = clamp(rint(x / s),
+// +-127) with the quotient rounded as an IEEE division; rows >= Lq code 0),
+// so for finite inputs the codes and scales are the same bits. Each wave
+// codes its own 32 rows (wrow0 ..) into the LDS Q tile; the two waves of a
+// 64-row block exchange their absmax through s_qmax (one slot per wave).
+// Every wave of the workgroup calls it (it holds a barrier). Returns the
+// block's s. Three shortcuts, exact for finite bf16 inputs:
+//  * the absmax is a packed 16-bit unsigned max of the bf16 bits with the
+//    sign cleared (finite magnitudes order like their bit patterns);
+//  * |x / s| < 127.5 for every finite bf16 x (s = RN(absmax / 127) is within
+//    2^-10 of absmax / 127 even when it is subnormal), so the clamp never
+//    binds, and adding 1.5 * 2^23 rounds the quotient to the nearest integer,
+//    ties to even, in one fp32 addition whose low byte is then the code;
+//  * the block's scale is read as a wave-uniform value, so the choice of
+//    quotient path is one branch.
 template <int D, int NW>
 __device__ __forceinline__ float q_code_tile(const uint16_t* __restrict__ qh, int Lq, int wrow0, uint8_t* s_q,
                                              float* s_qmax, int w, int lane) {
@@ -104,42 +113,64 @@ __device__ __forceinline__ float q_code_tile(const uint16_t* __restrict__ qh, in
       raw[j][0] = raw[j][1] = make_uint4(0, 0, 0, 0);
     }
   }
-  float amax = 0.0f;  // rows >= Lq hold zeros, which leave the absmax as it is
+  // Rows >= Lq hold zeros, which leave the absmax as it is.
+  typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+  v2u16 mx2 = {0, 0};
 #pragma unroll
   for (int j = 0; j < kPerLane; ++j)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      float f[8];
-      unpack8(raw[j][hf], f);
+      const uint4 u = raw[j][hf];
+      const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      for (int t = 0; t < 4; ++t)
+        mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(v2u16, ws[t] & 0x7FFF7FFFu));
     }
+  float amax = __uint_as_float((uint32_t)max(mx2[0], mx2[1]) << 16);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   if (lane == 0) s_qmax[w] = amax;
   __syncthreads();
-  const float am = fmaxf(s_qmax[w], s_qmax[w ^ 1]);
+  const float am = __uint_as_float(
+      __builtin_amdgcn_readfirstlane(__float_as_uint(fmaxf(s_qmax[w], s_qmax[w ^ 1]))));
   const float s = am / 127.0f;
-  const bool fast = s >= kFastDivMinScale;  // uniform over the block
-  const float r = fast ? 1.0f / s : 0.0f;
+  uint32_t cw[kPerLane][4];
+  // Codes of every chunk from the quotient function quot(x).
+  auto code_all = [&](auto quot) {
 #pragma unroll
-  for (int j = 0; j < kPerLane; ++j) {
-    uint32_t cw[4] = {0u, 0u, 0u, 0u};
-    if (am != 0.0f) {
+    for (int j = 0; j < kPerLane; ++j)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         float f[8];
         unpack8(raw[j][hf], f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float x = fast ? div_rn(f[i], s, r) : f[i] / s;
-          cw[2 * hf + (i >> 2)] |= code_i8(x) << (8 * (i & 3));
+        for (int g = 0; g < 2; ++g) {
+          uint32_t b[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) b[i] = __float_as_uint(quot(f[4 * g + i]) + 12582912.0f);
+          // low bytes of b0..b3 -> bytes 0..3
+          const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);
+          cw[j][2 * hf + g] = lo | hi;
         }
       }
-    }
+  };
+  if (am == 0.0f) {  // every code 0
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cw[j][t] = 0u;
+  } else if (s >= kFastDivMinScale) {
+    const float r = 1.0f / s;
+    code_all([&](float x) { return div_rn(x, s, r); });
+  } else {
+    code_all([&](float x) { return x / s; });
+  }
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
     const int p = lane + 64 * j;
     *reinterpret_cast<uint4*>(s_q + q_lds_off<D>(32 * w + p / kChunks, p % kChunks)) =
-        make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        make_uint4(cw[j][0], cw[j][1], cw[j][2], cw[j][3]);
   }
   return s;
 }

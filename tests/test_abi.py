@@ -31,7 +31,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("sage_quant_prep", "sage_quant_prep_noalloc", "sage_attn_fwd", "sage_attn_fwd_prepped",
-              "sage_attn_fwd_prepped_kernel", "sage_attn_fwd_kernel",
+              "sage_attn_fwd_prepped_kernel", "sage_attn_fwd_kernel", "sage_quant_prep_kv",
+              "sage_attn_fwd_kv_prepped", "sage_auto_design",
               "sage_workspace_bytes",
               "sage_prep_scratch_bytes", "sage_debug_qk_int32", "sage_debug_codecs", "sage_debug_epoch_trace",
               "sage_status_str"):
@@ -136,6 +137,39 @@ def test_prep_and_prepped_reject_bad_arguments(lib):
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 64, 0, 0.0, -1, None) == -1
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 64, 64, 0, 0.0, 2, None) == -1
     assert k(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 32, 0, 0.0, 1, None) == -2
+
+
+def test_kv_prep_and_kv_prepped_reject_bad_arguments(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.sage_prep_scratch_bytes(1, 1, 1, 64, 64, ctypes.byref(n)) == 0
+    p = lib.sage_quant_prep_kv
+    args = [FAKE, FAKE, 1, 1, 64, 64] + [FAKE] * 6 + [n.value, None]
+    assert p(*args[:6], None, *args[7:]) == -1                  # missing k_i8
+    short = list(args)
+    short[12] = n.value - 1
+    assert p(*short) == -3
+    assert p(FAKE, FAKE, 1, 1, 64, 96, *args[6:]) == -2          # unsupported D
+    odd = list(args)
+    odd[0] = ctypes.c_void_p((1 << 20) + 8)
+    assert p(*odd) == -1                                         # k not 16-byte aligned
+    a = lib.sage_attn_fwd_kv_prepped
+    ok = [FAKE] * 6 + [1, 1, 64, 64, 64, 0, 0.0, None]
+    assert a(*ok[:0], None, *ok[1:]) == -1                       # missing q
+    assert a(ctypes.c_void_p((1 << 20) + 2), *ok[1:]) == -1      # q not 16-byte aligned
+    assert a(*ok[:5], None, *ok[6:]) == -1                       # missing out
+    assert a(*ok[:10], 32, *ok[11:]) == -2                       # unsupported D
+    assert a(*ok[:11], 3, *ok[12:]) == -1                        # causal not 0/1
+
+
+def test_auto_design_reports_the_choice(lib):
+    d = ctypes.c_int(-1)
+    for shape, whole, want in [((2, 32, 4096, 4096, 128), 1, 5), ((2, 32, 4096, 4096, 128), 0, 1),
+                               ((1, 8, 1000, 1000, 128), 1, 2), ((1, 1, 128, 192, 128), 0, 2),
+                               ((4, 16, 8192, 8192, 64), 1, 5), ((1, 24, 32760, 32760, 128), 0, 1)]:
+        assert lib.sage_auto_design(*shape, whole, ctypes.byref(d)) == 0 and d.value == want, (shape, whole)
+    assert lib.sage_auto_design(1, 1, 64, 64, 96, 1, ctypes.byref(d)) == -2
+    assert lib.sage_auto_design(1, 1, 64, 64, 64, 2, ctypes.byref(d)) == -1
+    assert lib.sage_auto_design(1, 1, 64, 64, 64, 1, None) == -1
 
 
 def test_debug_qk_rejects_out_of_range_tiles(lib):

@@ -159,6 +159,44 @@ def test_entry_codes_q_blocks_at_the_scale_edges(gpu_device):
     assert np.array_equal(fused, entry)
 
 
+KV_SHAPES = [(1, 1, 1, 1, 64, False), (1, 2, 65, 63, 128, True), (2, 3, 200, 333, 128, True),
+             (1, 1, 1000, 64, 64, True), (1, 8, 300, 200, 128, False), (1, 1, 257, 1000, 64, False)]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lkv,D,causal", KV_SHAPES)
+def test_kv_prep_and_kv_prepped_equal_the_full_preparation_path(B, H, Lq, Lkv, D, causal, gpu_device):
+    """sage_quant_prep_kv writes the K/V operands of sage_quant_prep bit for
+    bit, and sage_attn_fwd_kv_prepped on them (bf16 Q coded in the main loop)
+    gives the fused design's output on sage_quant_prep's operands."""
+    say(f"kv prep + kv-prepped main loop vs full prep + fused: shape {(B, H, Lq, Lkv, D, causal)}")
+    q, k, v = (t.to(gpu_device) for t in si.make_qkv(B, H, Lq, Lkv, D, "normal", 2.0, seed=3 * Lq + Lkv))
+    full = sage.quant_prep(q, k, v)
+    kv = sage.quant_prep_kv(k, v)
+    torch.cuda.synchronize()
+    for n in ("k_i8", "k_scale", "k_mean", "v_fp8", "v_scale"):
+        assert torch.equal(full[n].view(torch.uint8) if full[n].dtype != torch.float32 else full[n].view(torch.int32),
+                           kv[n].view(torch.uint8) if kv[n].dtype != torch.float32 else kv[n].view(torch.int32)), n
+    sc = 1 / math.sqrt(D)
+    a = si.bf16_bits(sage.attn_fwd_prepped(full, causal, sc, kernel=FUSED))
+    b = si.bf16_bits(sage.attn_fwd_kv_prepped(q, kv, causal, sc))
+    c = si.bf16_bits(sage.attn_fwd_kv_prepped(q, full, causal, sc))  # K/V of the full preparation pass
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_whole_path_auto_uses_the_reported_design(gpu_device):
+    """sage_attn_fwd (automatic design) equals the design sage_auto_design
+    reports, run explicitly, and the fused design, bit for bit."""
+    for B, H, Lq, Lkv, D, causal in [(2, 32, 512, 512, 128, True), (1, 2, 300, 300, 64, False)]:
+        q, k, v = (t.to(gpu_device) for t in si.make_qkv(B, H, Lq, Lkv, D, "normal", 2.0, seed=Lq + D))
+        d = sage.auto_design(B, H, Lq, Lkv, D)
+        auto = si.bf16_bits(sage.attn_fwd(q, k, v, causal))
+        expl = si.bf16_bits(sage.attn_fwd(q, k, v, causal, kernel=d))
+        fused = si.bf16_bits(sage.attn_fwd(q, k, v, causal, kernel=FUSED))
+        torch.cuda.synchronize()
+        assert np.array_equal(auto, expl) and np.array_equal(auto, fused), (B, H, Lq, d)
+
+
 def test_persistent_counter_returns_to_zero_across_streams_and_shapes(gpu_device):
     """Launches of the persistent design alternate shapes (grids smaller than,
     equal to and larger than the resident workgroup count) and two streams;
