@@ -9,9 +9,11 @@
 //   finalize - per head: mean = fp32(sum / Lkv), sv = absmax / 448 (the
 //              splits spread over the workgroup);
 //   quant    - one read of Q, K, V per 64-row block: block absmax, codes.
-// With few splits per head (short keys) the finalize launch is skipped: each
-// K or V workgroup of the quantization pass reduces the splits of its head
-// itself, and the head's first K and V workgroups write the means and scales.
+// With few splits per head the finalize launch is skipped: each K or V
+// workgroup of the quantization pass reduces the splits of its head itself,
+// and the head's first K and V workgroups write the means and scales. With
+// short key sets the statistics launch is skipped as well: each K or V
+// workgroup of the quantization pass reduces its whole head (head_stats).
 // Every quotient is the correctly rounded fp32 (or fp64) one, as an IEEE
 // division gives. The K channel sums are fp64 sums over 256-row splits, then
 // over the splits: bf16 values carry 8 significant bits, so when a channel's
@@ -318,12 +320,77 @@ __device__ __forceinline__ float head_vscale(const PrepArgs& a, long bh, int c) 
   return m / 448.0f;
 }
 
+// Short key sets: a K or V quantization workgroup computes its head's
+// channel statistics itself, over all Lkv rows, with the statistics pass's
+// loop (fp64 channel sums of K, fp32 channel absmax of V), so the whole
+// preparation is one launch. Every K or V workgroup of a head reads the head
+// (from L2 after the first), so K and V are read NKB times over; this is
+// taken while those extra reads, (NKB - 1) * B * H * 2 * Lkv * D * 2 bytes,
+// stay within kSelfStatsMaxBytes (they then cost less than a launch: the
+// Q128 x KV192 fixture's preparation takes 6.3 instead of 9.3 us, while at
+// B1 H8 L1000, 60 MB over, it would take 14.3 instead of 10.6 us). The sums
+// are exact under the condition in the file header, so the means are the
+// statistics pass's bits. Results go to out[c] (the mean, or the V scale
+// absmax / 448) for every thread; red is the LDS area of the reduction.
+constexpr double kSelfStatsMaxBytes = 8.0 * 1024 * 1024;
+template <int D>
+union SelfStatsLds {
+  double sum[kThreads / (D / 8)][D];
+  float max[kThreads / (D / 8)][D];
+};
+template <int D, bool IS_K>
+__device__ void head_stats(const uint16_t* __restrict__ x, int L, SelfStatsLds<D>& red, float* out) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerIter = kThreads / kLanesPerRow;
+  constexpr int kBatch = 4;
+  const int tid = threadIdx.x;
+  const int cg = tid % kLanesPerRow, rg = tid / kLanesPerRow;
+  double s[8];
+  float mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { s[i] = 0.0; mx[i] = 0.0f; }
+  for (int t = rg; t < L; t += kBatch * kRowsPerIter) {
+    uint4 u[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int r = t + b * kRowsPerIter;
+      u[b] = r < L ? *reinterpret_cast<const uint4*>(x + (long)r * D + 8 * cg) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      float f[8];
+      unpack8(u[b], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (IS_K) s[i] += (double)f[i];
+        else mx[i] = fmaxf(mx[i], fabsf(f[i]));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (IS_K) red.sum[rg][8 * cg + i] = s[i];
+    else red.max[rg][8 * cg + i] = mx[i];
+  }
+  __syncthreads();
+  if (tid < D) {
+    double a = 0.0;
+    float m = 0.0f;
+    for (int r = 0; r < kRowsPerIter; ++r) {
+      if (IS_K) a += red.sum[r][tid];
+      else m = fmaxf(m, red.max[r][tid]);
+    }
+    out[tid] = IS_K ? (float)(a / (double)L) : m / 448.0f;
+  }
+}
+
 // One workgroup per (tensor, 64-row block): job in [0, nq) codes a Q block,
 // [nq, nq + nkb) a K block, [nq + nkb, nq + 2 nkb) a V block, with nq = nqb,
 // or 0 when the main loop codes Q itself (skip_q).
-template <int D>
+template <int D, bool SELF>
 __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
   __shared__ float s_red[4];
+  __shared__ SelfStatsLds<D> s_self;  // referenced (and allocated) only when SELF
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[D * kBlock];
   __shared__ float s_ch[D];  // K channel mean, or V channel scale
   __shared__ float s_rv[D];  // RN(1 / V channel scale)
@@ -343,7 +410,11 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
     const int blk = job - nq;
     Int8BlockLoad<D> ld;
     ld.load(a.k + bh * (long)a.Lkv * D, a.Lkv, blk);
-    if (threadIdx.x < D) {
+    if constexpr (SELF) {
+      head_stats<D, true>(a.k + bh * (long)a.Lkv * D, a.Lkv, s_self, s_ch);
+      __syncthreads();
+      if (blk == 0 && threadIdx.x < D) a.k_mean[bh * D + threadIdx.x] = s_ch[threadIdx.x];
+    } else if (threadIdx.x < D) {
       if (a.fuse_finalize) {
         const float mu = head_mean(a, bh, threadIdx.x);
         s_ch[threadIdx.x] = mu;
@@ -360,9 +431,16 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
     VBlockLoad<D> ld;
     ld.load(a.v + bh * (long)a.Lkv * D, a.Lkv, blk);
     bool tiny = false;
+    if constexpr (SELF) {
+      head_stats<D, false>(a.v + bh * (long)a.Lkv * D, a.Lkv, s_self, s_ch);
+      __syncthreads();
+    }
     if (threadIdx.x < D) {
       float s;
-      if (a.fuse_finalize) {
+      if constexpr (SELF) {
+        s = s_ch[threadIdx.x];
+        if (blk == 0) a.v_scale[bh * D + threadIdx.x] = s;
+      } else if (a.fuse_finalize) {
         s = head_vscale(a, bh, threadIdx.x);
         if (blk == 0) a.v_scale[bh * D + threadIdx.x] = s;
       } else {
@@ -380,35 +458,35 @@ __global__ __launch_bounds__(kThreads) void prep_quant_kernel(PrepArgs a) {
 
 int prep_n_split(int Lkv) { return (Lkv + kStatRows - 1) / kStatRows; }
 
+template <int D>
+static hipError_t launch_prep_t(PrepArgs a, hipStream_t stream) {
+  const int BH = a.B * a.H;
+  const int ns = a.n_split;
+  // The host bounds every flattened grid below 2^31 workgroups.
+  const dim3 g_stats((unsigned)((long)ns * BH)), g_fin((unsigned)((long)BH * (D / kFinChannels))),
+      g_quant((unsigned)((long)((a.skip_q ? 0 : a.nqb) + 2 * a.nkb) * BH));
+  if (a.self_stats) {
+    prep_quant_kernel<D, true><<<g_quant, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+  }
+  prep_stats_kernel<D><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (!a.fuse_finalize) {
+    prep_finalize_kernel<D><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  prep_quant_kernel<D, false><<<g_quant, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep(const PrepArgs& args, hipStream_t stream) {
   PrepArgs a = args;
-  const int BH = a.B * a.H;
-  const int ns = prep_n_split(a.Lkv);
-  a.n_split = ns;
-  a.fuse_finalize = ns <= kFuseMaxSplits;
-  // The host bounds both flattened grids below 2^31 workgroups.
-  const dim3 g_stats((unsigned)((long)ns * BH)), g_fin((unsigned)((long)BH * (a.D / kFinChannels))),
-      g_quant((unsigned)((long)((a.skip_q ? 0 : a.nqb) + 2 * a.nkb) * BH));
-  if (a.D == 128) {
-    prep_stats_kernel<128><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (!a.fuse_finalize) {
-      prep_finalize_kernel<128><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    prep_quant_kernel<128><<<g_quant, kThreads, 0, stream>>>(a);
-  } else {
-    prep_stats_kernel<64><<<g_stats, kThreads, 0, stream>>>(a.k, a.v, a.Lkv, ns, a.psum, a.pmax);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (!a.fuse_finalize) {
-      prep_finalize_kernel<64><<<g_fin, kThreads, 0, stream>>>(a.psum, a.pmax, ns, a.Lkv, a.k_mean, a.v_scale);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    prep_quant_kernel<64><<<g_quant, kThreads, 0, stream>>>(a);
-  }
-  return hipGetLastError();
+  a.n_split = prep_n_split(a.Lkv);
+  const double kv_bytes = 2.0 * a.B * a.H * (double)a.Lkv * a.D * 2;
+  a.self_stats = (a.nkb - 1) * kv_bytes <= kSelfStatsMaxBytes;
+  a.fuse_finalize = a.n_split <= kFuseMaxSplits;
+  return a.D == 128 ? launch_prep_t<128>(a, stream) : launch_prep_t<64>(a, stream);
 }
 
 }  // namespace sage

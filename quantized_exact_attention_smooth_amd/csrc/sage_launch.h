@@ -27,6 +27,7 @@ struct PrepArgs {
   int n_split;   // statistics splits per head
   int fuse_finalize;  // 1: the quantization workgroups reduce the splits themselves
   int skip_q;         // 1: Q is not coded (the main loop codes it from q)
+  int self_stats;     // 1: no statistics launch; K/V workgroups reduce their head themselves
 };
 
 struct AttnArgs {
