@@ -21,24 +21,28 @@
 //    each; K(e+1) and V(e+1) fill while epoch e computes), no staging
 //    registers.
 //  * QK: S^T = K . Q^T with v_mfma_i32_32x32x32_i8 (A = K rows from LDS,
-//    B = Q codes held in registers for the whole kernel). The K rows are
+//    B = Q codes from the workgroup's LDS Q tile, copied in once per tile,
+//    or coded there from bf16 Q by the entry design). The K rows are
 //    loaded in a permuted order so that each lane ends with 32 consecutive
 //    keys of ONE query: lane (h, q) holds S[q][32h .. 32h+31].
 //  * softmax: the row max is taken on the exact int32 scores (the dequant
 //    factor sq*sk*sm_scale*log2e is positive), then one cross-half exchange;
-//    p = exp2(fma(S, c, -m)) in fp32; the row sum stays a per-half partial
-//    until the epilogue.
+//    p = exp2(fma(S, c, -m)) in fp32 (relative to the integer row max once
+//    the scores are very large); the row sum stays a per-half partial until
+//    the epilogue.
 //  * P -> E4M3 in registers; that register block IS the B operand of the PV
 //    matrix-core step (O^T = V^T . P^T, v_mfma_f32_32x32x64_f8f6f4), so P
 //    never goes through LDS, and each lane's outputs belong to its own query.
 //  * two-level PV: RO *= alpha (skipped when no row max of the wave moved,
 //    i.e. alpha == 1 in every lane), then the matrix core reduces the epoch's
 //    64 keys in fp32 (inner level) and adds the result into RO, its C
-//    operand (outer level).
+//    operand (outer level); epoch 0 starts RO from a zero accumulator.
 //  * epilogue: r = 1/l (IEEE divide), out = bf16(RO * r * sv[c]) for rows < Lq,
 //    with sv read into LDS at the start; a wave's 32 rows are consecutive in
 //    memory, so they pass through LDS and leave as whole 16-byte chunks.
-//  * instantiations: TRACE records one wave's per-epoch state (debug).
+//  * instantiations: TRACE records one wave's per-epoch state (debug);
+//    PERSIST runs the tiles in persistent workgroups fed by work counters;
+//    NW = 8 gives 256-row workgroups; ENTRY codes the Q tile from bf16 Q.
 #include <type_traits>
 
 #include "attn_common.h"

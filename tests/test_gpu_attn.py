@@ -290,13 +290,23 @@ def test_large_scores_stay_finite_and_match_the_oracle(causal, gpu_device):
         assert_out_close(out[b, h], oracle_rows(o, causal, sc, 0, L), f"attn: large scores head {h}")
 
 
-def test_concurrent_calls_on_two_streams_match_sequential(gpu_device):
-    """Calls keep no state between them: two host threads, each on its own
+CONCURRENT_CASES = {
+    # small grids: the split design
+    "split": [((1, 4, 777, 777, 128), True, 11), ((2, 2, 300, 1025, 64), False, 12)],
+    # full grids (at least 256 tiles): the entry design, beside a small one
+    "entry": [((2, 32, 512, 512, 128), True, 13), ((1, 64, 512, 700, 64), False, 14),
+              ((1, 2, 300, 300, 128), True, 15)],
+}
+
+
+@pytest.mark.parametrize("which", sorted(CONCURRENT_CASES))
+def test_concurrent_calls_on_two_streams_match_sequential(which, gpu_device):
+    """Calls keep no state between them: host threads, each on its own
     stream (default priority), run different shapes at the same time, and
     every output equals the one from a sequential run bit for bit."""
     import threading
-    say("attn parity: concurrent calls on two streams")
-    cases = [((1, 4, 777, 777, 128), True, 11), ((2, 2, 300, 1025, 64), False, 12)]
+    say(f"attn parity: concurrent calls on separate streams ({which})")
+    cases = CONCURRENT_CASES[which]
     inputs = [tuple(t.to(gpu_device) for t in si.make_qkv(*shape, "normal", 2.0, seed))
               for shape, _, seed in cases]
     seq = []
@@ -328,14 +338,15 @@ def test_concurrent_calls_on_two_streams_match_sequential(gpu_device):
             np.testing.assert_array_equal(got, seq[i])
 
 
-def test_graph_replays_match_eager_runs(gpu_device):
+@pytest.mark.parametrize("B,H,L,D,causal", [(1, 3, 500, 128, True), (2, 32, 512, 128, True)])
+def test_graph_replays_match_eager_runs(B, H, L, D, causal, gpu_device):
     """sage_attn_fwd allocates nothing and issues no memset or host
     synchronisation, so a captured HIP graph of it replays correctly: four
     replays, with eager work and synchronisation between them and new input
     values copied in before some, each equal bit for bit to an eager call on
-    the same inputs."""
-    say("attn parity: HIP graph replays")
-    B, H, L, D, causal = 1, 3, 500, 128, True
+    the same inputs. The small shape runs the split design, the full grid the
+    entry design."""
+    say(f"attn parity: HIP graph replays, shape {(B, H, L, D, causal)}")
     sc = 1 / math.sqrt(D)
     q, k, v = (t.to(gpu_device) for t in si.make_qkv(B, H, L, L, D, "normal", 2.0, seed=21))
     ws = torch.empty(sage.workspace_bytes(B, H, L, L, D), dtype=torch.uint8, device=gpu_device)
