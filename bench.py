@@ -12,7 +12,8 @@ already resident in HBM. Prints one JSON line.
             stream the kernels run on), against the dense INT8/FP8
             matrix-core peak of MI355X (5.0 POPS);
   scopes    main (the step's main kernel alone: sage_attn_fwd_kv_prepped for
-            the entry design, else sage_attn_fwd_prepped), prep (its
+            the entry design, else sage_attn_fwd_prepped; with the entry design
+            sage_attn_fwd_prepped is also timed, as prepped_main), prep (its
             preparation pass: sage_quant_prep_kv, else sage_quant_prep) and
             end-to-end (sage_attn_fwd, the user-facing call) each timed as
             back-to-back launches; main also as the p50 and coefficient of
@@ -379,6 +380,22 @@ def main() -> int:
     main_avg = timed(main_loop)
     prep_avg = timed(prep)
     e2e_avg = timed(e2e)
+    prepped_avg = None
+    if entry:
+        # the prepared-operand main kernel (sage_attn_fwd_prepped, automatic
+        # design) on the same inputs, reported beside the step's own kernel
+        def full_prep():
+            _lib.check("sage_quant_prep", L.sage_quant_prep(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Lq, Lkv, D, q8.data_ptr(), qs.data_ptr(),
+                k8.data_ptr(), kscale.data_ptr(), kmean.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
+                scratch.data_ptr(), n.value, sp))
+
+        def prepped():
+            _lib.check("sage_attn_fwd_prepped", L.sage_attn_fwd_prepped(
+                q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), kscale.data_ptr(), v8.data_ptr(), vscale.data_ptr(),
+                out.data_ptr(), B, H, Lq, Lkv, D, causal, w.sm_scale, sp))
+        full_prep()
+        prepped_avg = timed(prepped)
 
     # main kernel: p50 / CV of 10 batches of 20 launches, p50 of single launches
     batches = []
@@ -433,6 +450,10 @@ def main() -> int:
         "prep_frac_hbm": prep_bytes / (prep_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "e2e_ms": e2e_avg, "e2e_tops": ops / (e2e_avg * 1e-3) / 1e12,
     }
+    if prepped_avg is not None:
+        rec["prepped_main"] = {"call": "sage_attn_fwd_prepped (automatic design: fused)", "ms": prepped_avg,
+                               "tops": ops / (prepped_avg * 1e-3) / 1e12,
+                               "frac": ops / (prepped_avg * 1e-3) / 1e12 / PEAK_TOPS}
     if args.workload is None and not args.shape:
         rec["fixture_q128_kv192"] = fixture_latency(L, dev, stream)
     if not args.no_cpu_baseline:
