@@ -115,8 +115,9 @@ int sage_quant_prep_noalloc(const void* q, const void* k, const void* v, int B, 
                             uint8_t* v_fp8, float* v_scale, void* stream);
 
 /*
- * Attention from prepared operands (the fused main loop alone), in the
- * layouts sage_quant_prep writes. Per query row i, strictly ascending 64-key
+ * Attention from prepared operands (the main loop alone, in the design
+ * SAGE_KERNEL_AUTO selects for prepared operands), in the layouts
+ * sage_quant_prep writes. Per query row i, strictly ascending 64-key
  * epochs (Experiment Log, "Phase 1 State-Ownership Decision"):
  *   S = q8 . k8 (exact int32), z = S * sq * sk * sm_scale, online max m and
  *   sum l, alpha = exp(m_old - m_new), P8 = e4m3(exp(z - m_new)),

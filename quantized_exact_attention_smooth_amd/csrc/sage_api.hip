@@ -146,7 +146,8 @@ void* static_scratch(int* status) {
   return addr[dev];
 }
 
-// The main-loop design SAGE_KERNEL_AUTO selects. When the grid has fewer
+// The main-loop design SAGE_KERNEL_AUTO selects on prepared operands. When
+// the grid has fewer
 // 128-row tiles than the GPU has compute units, the wave-specialised design
 // finishes each tile sooner (twice the waves per tile: 0.0180 against
 // 0.0204 ms at B1 H8 L1000 D128 causal); on full grids the fused design is
