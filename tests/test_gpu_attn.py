@@ -138,7 +138,11 @@ def test_zero_q_constant_v_is_exact(L, D, causal, gpu_device):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_one_hot_keys_exact(D, causal, gpu_device):
+@pytest.mark.parametrize("q_scale", [1.0, 2.0 ** 100])
+def test_one_hot_keys_exact(D, causal, q_scale, gpu_device):
+    """Query i matches key i only, so out[i] is exactly the dequantized V row
+    i; with Q times 2^100 the scores reach about 2^108 (the large-score
+    exponent path) and the result must be the same."""
     L = D
     rng = np.random.default_rng(D + causal)
     perm = rng.permutation(D)
@@ -147,9 +151,10 @@ def test_one_hot_keys_exact(D, causal, gpu_device):
     vv = (rng.uniform(0.5, 1.0, (L, D)) * rng.choice([-1, 1], (L, D))).astype(np.float32)
     vv[0, :] = 1.0
     t = lambda x: torch.from_numpy(x).to(torch.bfloat16).reshape(1, 1, L, D)
-    say(f"one-hot keys: D={D} causal={causal}")
-    out = _gpu_out(t(qk), t(qk), t(vv), causal, 1 / math.sqrt(D), gpu_device)
-    p = oracle.prep_head(si.bf16_bits(t(qk))[0, 0], si.bf16_bits(t(qk))[0, 0], si.bf16_bits(t(vv))[0, 0])
+    qq = qk * np.float32(q_scale)
+    say(f"one-hot keys: D={D} causal={causal} Q scale {q_scale}")
+    out = _gpu_out(t(qq), t(qk), t(vv), causal, 1 / math.sqrt(D), gpu_device)
+    p = oracle.prep_head(si.bf16_bits(t(qq))[0, 0], si.bf16_bits(t(qk))[0, 0], si.bf16_bits(t(vv))[0, 0])
     dec = oracle.e4m3_decode(p["v8"][:L]).astype(np.float32)
     want = oracle.bf16_round(dec * p["v_scale"][None, :])
     assert np.array_equal(out[0, 0], want)

@@ -154,6 +154,28 @@ def test_one_hot_keys_select_one_value_row(D, causal):
     np.testing.assert_array_equal(out, expect)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_one_hot_keys_at_huge_scores_stay_exact(D):
+    """The same one-hot rows with Q scaled by 2^100 (exact in bf16): scores
+    reach about 2^108, every other key (negative after smoothing) is below the
+    top by a comparable amount, and p = exp(z - m) is 1 for the top key and 0
+    for the rest, so the output is again exactly the dequantized V row and
+    finite (the reading for very large scores: every p <= 1)."""
+    L = D
+    rng = np.random.default_rng(3 * D)
+    perm = rng.permutation(D)
+    k = np.zeros((L, D), np.float32)
+    k[np.arange(L), perm] = 16.0
+    q = k * np.float32(2.0 ** 100)
+    v = rng.uniform(0.5, 1.0, (L, D)) * rng.choice([-1, 1], (L, D))
+    p = oracle.prep_head(_bits(q), _bits(k), _bits(v))
+    assert float(p["q_scale"][0]) > 2.0 ** 90
+    for causal in (False, True):
+        out = oracle.attn_rows(p, causal, 1 / math.sqrt(D))
+        dec = oracle.e4m3_decode(p["v8"][:L]).astype(np.float32)
+        np.testing.assert_array_equal(out, _bits(dec * p["v_scale"][None, :]))
+
+
 def test_rows_without_visible_keys_output_zero():
     Lq, Lkv, D = 130, 64, 64
     q, k, v = _f64_head(Lq, Lkv, D, seed=3)
