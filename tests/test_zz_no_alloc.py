@@ -46,8 +46,15 @@ def _bits(t):
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
-@pytest.mark.parametrize("first,second", [((2, 3, 1000, 1300, 128, "normal"), (1, 2, 200, 300, 64, "normal")),
+# The second call of each pair is smaller than the first. In the first two
+# pairs both calls take the two-pass preparation, which uses the scratch
+# (the second call's is a finalize launch, or the finalize folded into the
+# quantization pass: at most 4 splits). The third pair's second call is a
+# short key set, prepared in one launch without the scratch.
+@pytest.mark.parametrize("first,second", [((2, 3, 1000, 1300, 128, "normal"), (1, 2, 1000, 1100, 64, "normal")),
                                           ((1, 4, 4096, 4096, 128, "normal"),
+                                           (1, 4, 500, 1000, 128, "student_t_outlier")),
+                                          ((1, 2, 2000, 2100, 128, "normal"),
                                            (1, 1, 65, 130, 128, "student_t_outlier"))])
 def test_noalloc_prep_equals_prep_on_two_calls(first, second, gpu_device):
     for i, (B, H, Lq, Lkv, D, dist) in enumerate((first, second)):
