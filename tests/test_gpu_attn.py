@@ -71,7 +71,9 @@ SHAPES = [(1, 1, 1, 1, 64, False), (1, 1, 1, 1, 128, True), (1, 2, 63, 63, 64, T
           (1, 1, 65, 65, 128, True), (1, 2, 127, 129, 64, False), (1, 1, 129, 127, 128, True),
           (2, 3, 200, 333, 128, True), (1, 1, 1000, 64, 64, True), (1, 1, 64, 1000, 128, True),
           (1, 1, 191, 193, 64, False), (1, 2, 300, 300, 128, True), (1, 1, 257, 1, 128, False),
-          (1, 1, 384, 384, 64, True)]
+          (1, 1, 384, 384, 64, True),
+          # a few query rows against many keys (decode-like): 64 epochs in one workgroup per head
+          (1, 4, 16, 4096, 128, False), (1, 2, 1, 4096, 64, True), (2, 2, 33, 4000, 128, True)]
 
 
 @pytest.mark.parametrize("B,H,Lq,Lkv,D,causal", SHAPES)
