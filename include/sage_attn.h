@@ -289,6 +289,17 @@ int sage_debug_epoch_trace(const int8_t* q_i8, const float* q_scale, const int8_
                            int h, int row0, float* stats, uint8_t* p8, float* pv, float* ro, void* stream);
 
 /*
+ * Debug: the same per-epoch checkpoints for the entry design's main loop
+ * (sage_attn_fwd_kv_prepped: bf16 q, coded into the Q tile by the loop
+ * itself) on K/V prepared by sage_quant_prep_kv or sage_quant_prep; the
+ * records and the other arguments as sage_debug_epoch_trace.
+ */
+int sage_debug_epoch_trace_kv(const void* q, const int8_t* k_i8, const float* k_scale, const uint8_t* v_fp8,
+                              const float* v_scale, void* out, int B, int H, int Lq, int Lkv, int D, int causal,
+                              float sm_scale, int b, int h, int row0, float* stats, uint8_t* p8, float* pv,
+                              float* ro, void* stream);
+
+/*
  * Debug: run the device conversions the main loop uses on n fp32 values x
  * (device): p8[i] = FP8 E4M3FN code as the probability packing produces it,
  * bf16[i] = bf16 bits as the output conversion produces them.

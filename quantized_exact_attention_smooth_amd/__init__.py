@@ -18,7 +18,7 @@ from ._lib import (LIB_PATH, SAGE_BLOCK, SAGE_KERNEL_AUTO, SAGE_KERNEL_ENTRY, SA
 
 __all__ = ["workspace_bytes", "prep_scratch_bytes", "quant_prep", "attn_fwd_prepped", "attn_fwd", "quant_prep_kv",
            "attn_fwd_kv_prepped", "auto_design",
-           "debug_qk_int32", "debug_codecs", "debug_epoch_trace", "SageError", "status_str", "LIB_PATH",
+           "debug_qk_int32", "debug_codecs", "debug_epoch_trace", "debug_epoch_trace_kv", "SageError", "status_str", "LIB_PATH",
            "SAGE_KERNEL_AUTO", "SAGE_KERNEL_FUSED", "SAGE_KERNEL_SPLIT", "SAGE_KERNEL_PERSISTENT", "SAGE_KERNEL_WIDE",
            "SAGE_KERNEL_ENTRY"]
 
@@ -201,6 +201,30 @@ def debug_epoch_trace(prep: dict, b: int, h: int, row0: int, causal: bool, sm_sc
         float(sm_scale) if sm_scale else 0.0, int(kernel), int(b), int(h), int(row0), stats.data_ptr(),
         p8.data_ptr(), pv.data_ptr(), ro.data_ptr(), _stream(stream))
     check("sage_debug_epoch_trace", st)
+    return dict(stats=stats, p8=p8, pv=pv, ro=ro, out=out)
+
+
+def debug_epoch_trace_kv(q: torch.Tensor, kv: dict, b: int, h: int, row0: int, causal: bool,
+                         sm_scale: float = None, stream=None) -> dict:
+    """sage_debug_epoch_trace_kv: the checkpoints of debug_epoch_trace for the
+    entry design's main loop (bf16 q against the K/V operands of
+    quant_prep_kv or quant_prep)."""
+    B, H, Lkv, D = kv["kv_shape"] if "kv_shape" in kv else (*kv["shape"][:2], *kv["shape"][3:])
+    Lq = q.shape[2]
+    nkb = -(-Lkv // SAGE_BLOCK)
+    dev = q.device
+    stats = torch.full((32, nkb + 1, 4), float("nan"), dtype=torch.float32, device=dev)
+    p8 = torch.full((32, nkb, SAGE_BLOCK), 0xFF, dtype=torch.uint8, device=dev)
+    pv = torch.full((32, nkb, D), float("nan"), dtype=torch.float32, device=dev)
+    ro = torch.full((32, nkb, D), float("nan"), dtype=torch.float32, device=dev)
+    out = torch.zeros((B, H, Lq, D), dtype=torch.bfloat16, device=dev)
+    st = lib().sage_debug_epoch_trace_kv(
+        _dev(q, torch.bfloat16, "q"), _dev(kv["k_i8"], torch.int8, "k_i8"),
+        _dev(kv["k_scale"], torch.float32, "k_scale"), _dev(kv["v_fp8"], torch.uint8, "v_fp8"),
+        _dev(kv["v_scale"], torch.float32, "v_scale"), _dev(out, torch.bfloat16, "out"), B, H, Lq, Lkv, D,
+        int(bool(causal)), float(sm_scale) if sm_scale else 0.0, int(b), int(h), int(row0), stats.data_ptr(),
+        p8.data_ptr(), pv.data_ptr(), ro.data_ptr(), _stream(stream))
+    check("sage_debug_epoch_trace_kv", st)
     return dict(stats=stats, p8=p8, pv=pv, ro=ro, out=out)
 
 

@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             L.sage_debug_epoch_trace.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, I, P, P, P, P,
                                                  P]
             L.sage_debug_epoch_trace.restype = I
+            L.sage_debug_epoch_trace_kv.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, I, P, P, P, P, P]
+            L.sage_debug_epoch_trace_kv.restype = I
             _lib = L
     return _lib
 

@@ -500,6 +500,7 @@ hipError_t launch_attn(const AttnArgs& a, int D, bool causal, int kernel, hipStr
 }
 hipError_t launch_attn_trace(const AttnArgs& a, int D, bool causal, int kernel, hipStream_t stream) {
   if (kernel == kKernelSplit) return launch_attn_split(a, D, causal, true, stream);
+  if (kernel == kKernelEntry) return launch_attn_v<true, false, 4, true>(a, D, causal, stream);
   if (kernel == kKernelWide) return launch_attn_wide(a, D, causal, true, stream);
   return launch_attn_fused(a, D, causal, true, stream);
 }

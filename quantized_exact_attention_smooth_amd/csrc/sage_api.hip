@@ -351,30 +351,51 @@ int sage_attn_fwd_prepped(const int8_t* q_i8, const float* q_scale, const int8_t
                                       causal, sm_scale, SAGE_KERNEL_AUTO, stream);
 }
 
+// The trace record setup shared by the two trace entry points.
+int trace_setup(sage::AttnArgs* a, int kind, int H, int Lq, int B, int b, int h, int row0, float* stats,
+                uint8_t* p8, float* pv, float* ro) {
+  set_tiles(a, kind);
+  if (b < 0 || b >= B || h < 0 || h >= H || row0 < 0 || row0 >= Lq || row0 % 32 != 0) return SAGE_ERR_INVALID_ARG;
+  if (!stats || !p8 || !pv || !ro || misaligned(stats, 16) || misaligned(p8, 4) || misaligned(pv, 4) ||
+      misaligned(ro, 4))
+    return SAGE_ERR_INVALID_ARG;
+  a->trace_bh = b * H + h;
+  a->trace_tile = row0 / sage::tile_rows(kind);
+  a->trace_wave = (row0 % sage::tile_rows(kind)) / 32;
+  a->tr_stats = stats;
+  a->tr_p8 = p8;
+  a->tr_pv = pv;
+  a->tr_ro = ro;
+  return SAGE_OK;
+}
+
 int sage_debug_epoch_trace(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
                            const uint8_t* v_fp8, const float* v_scale, void* out, int B, int H, int Lq, int Lkv,
                            int D, int causal, float sm_scale, int kernel, int b, int h, int row0, float* stats,
                            uint8_t* p8, float* pv, float* ro, void* stream) {
   sage::AttnArgs a;
-  const int st = attn_args(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, out, B, H, Lq, Lkv, D, causal,
-                           sm_scale, &a);
+  int st = attn_args(q_i8, q_scale, k_i8, k_scale, v_fp8, v_scale, out, B, H, Lq, Lkv, D, causal, sm_scale, &a);
   if (st != SAGE_OK) return st;
   int kind = resolve_kernel(kernel, B, H, Lq);
   if (kind < 0 || kind == sage::kKernelEntry) return SAGE_ERR_INVALID_ARG;
   if (kind == sage::kKernelPersistent) kind = sage::kKernelFused;  // the same tile code, traced on one tile
-  set_tiles(&a, kind);
-  if (b < 0 || b >= B || h < 0 || h >= H || row0 < 0 || row0 >= Lq || row0 % 32 != 0) return SAGE_ERR_INVALID_ARG;
-  if (!stats || !p8 || !pv || !ro || misaligned(stats, 16) || misaligned(p8, 4) || misaligned(pv, 4) ||
-      misaligned(ro, 4))
-    return SAGE_ERR_INVALID_ARG;
-  a.trace_bh = b * H + h;
-  a.trace_tile = row0 / sage::tile_rows(kind);
-  a.trace_wave = (row0 % sage::tile_rows(kind)) / 32;
-  a.tr_stats = stats;
-  a.tr_p8 = p8;
-  a.tr_pv = pv;
-  a.tr_ro = ro;
+  st = trace_setup(&a, kind, H, Lq, B, b, h, row0, stats, p8, pv, ro);
+  if (st != SAGE_OK) return st;
   return hip_status(sage::launch_attn_trace(a, D, causal == 1, kind, (hipStream_t)stream));
+}
+
+int sage_debug_epoch_trace_kv(const void* q, const int8_t* k_i8, const float* k_scale, const uint8_t* v_fp8,
+                              const float* v_scale, void* out, int B, int H, int Lq, int Lkv, int D, int causal,
+                              float sm_scale, int b, int h, int row0, float* stats, uint8_t* p8, float* pv,
+                              float* ro, void* stream) {
+  if (!q) return SAGE_ERR_INVALID_ARG;
+  sage::AttnArgs a;
+  int st = attn_args(nullptr, nullptr, k_i8, k_scale, v_fp8, v_scale, out, B, H, Lq, Lkv, D, causal, sm_scale,
+                     &a, q);
+  if (st != SAGE_OK) return st;
+  st = trace_setup(&a, sage::kKernelEntry, H, Lq, B, b, h, row0, stats, p8, pv, ro);
+  if (st != SAGE_OK) return st;
+  return hip_status(sage::launch_attn_trace(a, D, causal == 1, sage::kKernelEntry, (hipStream_t)stream));
 }
 
 int sage_attn_fwd_kernel(const void* q, const void* k, const void* v, void* out, int B, int H, int Lq, int Lkv,

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("sage_quant_prep", "sage_quant_prep_noalloc", "sage_attn_fwd", "sage_attn_fwd_prepped",
               "sage_attn_fwd_prepped_kernel", "sage_attn_fwd_kernel", "sage_quant_prep_kv",
-              "sage_attn_fwd_kv_prepped", "sage_auto_design",
+              "sage_attn_fwd_kv_prepped", "sage_auto_design", "sage_debug_epoch_trace_kv",
               "sage_workspace_bytes",
               "sage_prep_scratch_bytes", "sage_debug_qk_int32", "sage_debug_codecs", "sage_debug_epoch_trace",
               "sage_status_str"):
@@ -188,4 +188,10 @@ def test_debug_qk_rejects_out_of_range_tiles(lib):
     assert t(*ok, 2, 0, 0, 0, FAKE, FAKE, None, FAKE, None) == -1       # missing pv
     assert t(*ok, 5, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1       # entry design: not traced
     assert t(*ok, 6, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1       # unknown design
+    tk = lib.sage_debug_epoch_trace_kv
+    okk = [FAKE] * 6 + [2, 3, 128, 128, 64, 1, 0.0]
+    assert tk(None, *okk[1:], 0, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1      # missing q
+    assert tk(*okk, 2, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == -1                # b out of range
+    assert tk(*okk, 0, 0, 16, FAKE, FAKE, FAKE, FAKE, None) == -1               # row0 not a multiple of 32
+    assert tk(*okk, 0, 0, 0, FAKE, FAKE, None, FAKE, None) == -1                # missing pv
     assert lib.sage_debug_codecs(FAKE, 0, FAKE, FAKE, None) == 0

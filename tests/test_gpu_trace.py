@@ -1,7 +1,8 @@
 """Per-epoch checkpoints of the main loop against the oracle's own (Experiment
 Log, "Phase 2B Fixed Aligned Numerical Prototype": the m, d, FP8 probability,
 rescale, PV, FP32 RO and reciprocal checkpoints, here after every epoch), for
-each main-loop design.
+each main-loop design (the entry design through sage_debug_epoch_trace_kv,
+with bf16 Q coded by the loop).
 
 sage_debug_epoch_trace runs the main kernel itself on one tile and records the
 state of 32 rows after each epoch it computes. Against oracle.attn_row_trace
@@ -49,7 +50,8 @@ CASES = {
 }
 
 
-KERNELS = {"fused": sage.SAGE_KERNEL_FUSED, "split": sage.SAGE_KERNEL_SPLIT, "wide": sage.SAGE_KERNEL_WIDE}
+KERNELS = {"fused": sage.SAGE_KERNEL_FUSED, "split": sage.SAGE_KERNEL_SPLIT, "wide": sage.SAGE_KERNEL_WIDE,
+           "entry": sage.SAGE_KERNEL_ENTRY}
 
 
 @pytest.mark.parametrize("kernel", sorted(KERNELS))
@@ -58,15 +60,22 @@ def test_epoch_checkpoints_match_the_oracle(wi, kernel, gpu_device):
     w = si.WORKLOADS[wi]
     say(f"epoch trace ({kernel}): {w.name} rows {CASES[wi]}")
     q, k, v = si.workload_qkv(w)
-    pr = sage.quant_prep(q.to(gpu_device), k.to(gpu_device), v.to(gpu_device))
-    full = sage.attn_fwd_prepped(pr, w.causal, w.sm_scale, kernel=KERNELS[kernel])
+    qd = q.to(gpu_device)
+    pr = sage.quant_prep(qd, k.to(gpu_device), v.to(gpu_device))
+    if kernel == "entry":  # bf16 Q, coded by the main loop, against the prepared K/V
+        full = sage.attn_fwd_kv_prepped(qd, pr, w.causal, w.sm_scale)
+    else:
+        full = sage.attn_fwd_prepped(pr, w.causal, w.sm_scale, kernel=KERNELS[kernel])
     torch.cuda.synchronize()
     full_bits = si.bf16_bits(full)
     preps = oracle_preps(q, k, v, sorted({(b, h) for b, h, _ in CASES[wi]}))
     nkb = -(-w.Lkv // 64)
     p8_total = p8_diff = 0
     for b, h, row0 in CASES[wi]:
-        t = sage.debug_epoch_trace(pr, b, h, row0, w.causal, w.sm_scale, kernel=KERNELS[kernel])
+        if kernel == "entry":
+            t = sage.debug_epoch_trace_kv(qd, pr, b, h, row0, w.causal, w.sm_scale)
+        else:
+            t = sage.debug_epoch_trace(pr, b, h, row0, w.causal, w.sm_scale, kernel=KERNELS[kernel])
         torch.cuda.synchronize()
         st, p8, ro = t["stats"].cpu().numpy(), t["p8"].cpu().numpy(), t["ro"].cpu().numpy()
         pv = t["pv"].cpu().numpy()
