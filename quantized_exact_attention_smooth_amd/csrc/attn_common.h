@@ -1,6 +1,7 @@
 // Device code shared by the main-loop kernels (internal header): the QK
-// matrix-core step, the row reductions, the E4M3 and bf16 packing and the
-// direct global-to-LDS tile copies.
+// matrix-core step, the row reductions, the E4M3 and bf16 packing, the
+// direct global-to-LDS tile copies, the online softmax of one epoch, the PV
+// step, the epilogue's output staging and the checkpoint records.
 #pragma once
 
 #include <limits.h>
